@@ -1,0 +1,12 @@
+"""Row-wise INT4/INT8 quantized embedding tables on MI355X (gfx950).
+
+The compute lives in a HIP C-ABI library (``libqemb.so``, declared in
+``include/qemb.h``); :mod:`int4_row_wise_amd.qemb` is a thin ctypes binding
+over it that only marshals torch tensors and the current stream.  The
+library loads on first use and raises if it was not built; there is no CPU
+fallback.  :mod:`int4_row_wise_amd.synth` draws the seeded synthetic inputs.
+"""
+from .qemb import (  # noqa: F401
+    RANGE, GREEDY, SUM, WEIGHTED_SUM, QembError, abi_version, bag_forward, dequantize,
+    l2_error, load_library, quantize_rowwise, row_stride,
+)

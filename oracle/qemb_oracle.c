@@ -1,0 +1,512 @@
+/*
+ * qemb_oracle.c -- plain, slow CPU oracle for row-wise quantized embeddings.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library under int4_row_wise_amd/) never calls, links or includes
+ * anything here, and this file includes nothing from it.
+ *
+ * What it computes, and where each step comes from:
+ *
+ *  - Row-wise uniform quantization with a per-row scale and bias, clipped
+ *    either to the row's range or to thresholds found by a greedy search over
+ *    the row's squared error ("Post-Training 4-bit Quantization on Embedding
+ *    Tables", review page, sections "Proposed method" and "Main findings").
+ *  - Scale and bias stored as binary16 (same page, "Proposed method": fp16
+ *    storage of scale and bias; "Main findings": 13.28% of fp32 size at d=128).
+ *  - Two 4-bit codes packed per byte (DQRM repository page, paragraph on the
+ *    Android demo: INT4 vectors must be bit-packed into INT8 storage).
+ *  - Pooled embedding-bag lookup of sparse categorical ids ("Deep Learning
+ *    Recommendation Model for Personalization and Recommendation Systems",
+ *    review page, "Proposed method": embedding tables map sparse inputs to
+ *    dense vectors), with sum or weighted-sum pooling over CSR bags.
+ *  - Normalized l2 error of the quantized rows (Post-Training 4-bit page,
+ *    "Proposed method": quantization error measured by a normalized l2 loss).
+ *
+ * The pages give no formulas.  The numeric rules used here (binary32 RNE with
+ * one rounding per written operation, no contraction, IEEE division, fp16
+ * round-to-nearest-even, ties-to-even code rounding, the contiguous-halves
+ * pairwise sum for the row error, the shrink-from-either-end greedy walk) are
+ * readings of those passages; the project's design notes list each one.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math -fopenmp -shared
+ *        -fPIC.  x86-64 SSE arithmetic has no excess precision.
+ * OpenMP is used only across independent rows and bags with a static
+ * schedule, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OR_OK 0
+#define OR_INVALID -1
+#define OR_PRECONDITION -5
+
+#define OR_MAX_DIM 4096
+
+/* ------------------------------------------------------------------ */
+/* binary16 <-> binary32, written out from the IEEE-754 encodings.      */
+/* ------------------------------------------------------------------ */
+
+static uint32_t bits_of(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return u;
+}
+
+static float float_of(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Round a binary32 value to the nearest binary16 value, ties to even. */
+static uint16_t to_half(float f) {
+  uint32_t u = bits_of(f);
+  uint32_t sign = (u >> 16) & 0x8000u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a >= 0x7f800000u) {              /* inf or nan */
+    return (uint16_t)(sign | 0x7c00u | (a > 0x7f800000u ? 0x0200u : 0u));
+  }
+  int e = (int)(a >> 23);              /* biased binary32 exponent */
+  uint32_t mant = a & 0x7fffffu;
+  if (e >= 113) {                      /* |f| >= 2^-14: binary16 normal range */
+    if (e > 142) return (uint16_t)(sign | 0x7c00u);  /* >= 2^16: overflow */
+    uint32_t base = ((uint32_t)(e - 112) << 10) | (mant >> 13);
+    uint32_t rem = mant & 0x1fffu;
+    if (rem > 0x1000u || (rem == 0x1000u && (base & 1u))) base += 1u;
+    if (base >= 0x7c00u) base = 0x7c00u;  /* rounded past the largest finite */
+    return (uint16_t)(sign | base);
+  }
+  /* Below 2^-14: result is a binary16 subnormal (units of 2^-24) or zero.
+     value = mant24 * 2^(e-150) = mant24 * 2^(e-126) units of 2^-24. */
+  if (e == 0) return (uint16_t)sign;   /* binary32 subnormal: far below 2^-25 */
+  int shift = 126 - e;                 /* >= 14 */
+  if (shift > 24) return (uint16_t)sign;
+  uint32_t mant24 = mant | 0x800000u;
+  uint32_t q = mant24 >> shift;
+  uint32_t rem = mant24 & ((1u << shift) - 1u);
+  uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (q & 1u))) q += 1u;
+  return (uint16_t)(sign | q);
+}
+
+/* Exact binary16 -> binary32. */
+static float from_half(uint16_t h) {
+  uint32_t sign = ((uint32_t)h & 0x8000u) << 16;
+  uint32_t E = ((uint32_t)h >> 10) & 0x1fu;
+  uint32_t m = (uint32_t)h & 0x3ffu;
+  if (E == 0) {
+    float v = ldexpf((float)m, -24);   /* exact: m < 2^10 */
+    return sign ? -v : v;
+  }
+  if (E == 31) return float_of(sign | 0x7f800000u | (m << 13));
+  return float_of(sign | ((E + 112u) << 23) | (m << 13));
+}
+
+/* ------------------------------------------------------------------ */
+/* Row layout                                                          */
+/* ------------------------------------------------------------------ */
+
+/* Code bytes of one row: two 4-bit codes per byte, or one 8-bit code. */
+static int64_t code_bytes(int dim, int bits) {
+  return ((int64_t)dim * bits + 7) / 8;
+}
+
+/* Row stride: codes, fp16 scale, fp16 bias, zero padding to 16 bytes. */
+int64_t oracle_row_stride(int dim, int bits) {
+  if (dim < 1 || (bits != 4 && bits != 8)) return -1;
+  int64_t raw = code_bytes(dim, bits) + 4;
+  return (raw + 15) / 16 * 16;
+}
+
+/* ------------------------------------------------------------------ */
+/* One row: range, parameters, codes, dequantized values, error.       */
+/* ------------------------------------------------------------------ */
+
+/* Row range (min and max), with -0 folded to +0 by adding +0. */
+static void row_range(const float* x, int d, float* lo, float* hi) {
+  float mn = x[0], mx = x[0];
+  for (int i = 1; i < d; ++i) {
+    if (x[i] < mn) mn = x[i];
+    if (x[i] > mx) mx = x[i];
+  }
+  *lo = mn + 0.0f;
+  *hi = mx + 0.0f;
+}
+
+/* Parameters for the clipping window [lo, hi]: the scale is the window over
+   Q = 2^bits - 1 steps and the bias is the window's low end, both rounded to
+   binary16; the codes are computed against the stored (rounded) values. */
+typedef struct {
+  uint16_t s16, b16;
+  float sf, bf;
+} params_t;
+
+static params_t make_params(float lo, float hi, int Q) {
+  params_t p;
+  float s = (hi - lo) / (float)Q;
+  if (!(s > 0.0f)) s = 0.0f;
+  p.s16 = to_half(s);
+  p.b16 = to_half(lo);
+  p.sf = from_half(p.s16);
+  p.bf = from_half(p.b16);
+  return p;
+}
+
+/* Integer code of one element: round-half-even of (x - bias) * (1/scale),
+   clamped to [0, Q]; every code is 0 when the stored scale is 0. */
+static int code_of(float x, params_t p, float r, int Q) {
+  if (p.sf == 0.0f) return 0;
+  float t = (x - p.bf) * r;
+  float q = rintf(t);
+  if (q < 0.0f) q = 0.0f;
+  if (q > (float)Q) q = (float)Q;
+  return (int)q;
+}
+
+/* Dequantized value of code q: scale * q + bias with a single rounding. */
+static float dequant_value(float sf, float bf, int q) {
+  return fmaf(sf, (float)q, bf);
+}
+
+/* Pairwise sum over contiguous halves of a power-of-two length n. */
+static float pairwise_sum(const float* u, int n) {
+  if (n == 1) return u[0];
+  int h = n / 2;
+  return pairwise_sum(u, h) + pairwise_sum(u + h, h);
+}
+
+static int next_pow2(int d) {
+  int n = 1;
+  while (n < d) n <<= 1;
+  return n;
+}
+
+/* Sum of squared errors of the row encoded with window [lo, hi]. */
+static float window_sse(const float* x, int d, float lo, float hi, int Q) {
+  float u[OR_MAX_DIM];
+  int n = next_pow2(d);
+  params_t p = make_params(lo, hi, Q);
+  float r = (p.sf == 0.0f) ? 0.0f : 1.0f / p.sf;
+  for (int i = 0; i < d; ++i) {
+    int q = code_of(x[i], p, r, Q);
+    float e = x[i] - dequant_value(p.sf, p.bf, q);
+    u[i] = e * e;
+  }
+  for (int i = d; i < n; ++i) u[i] = 0.0f;
+  return pairwise_sum(u, n);
+}
+
+/* Greedy clip search.  The window starts at the row's range and moves one
+   step of width (max - min) / n_bins at a time, from whichever end gives the
+   lower squared error (ties move the high end); after n_steps moves, the
+   window with the lowest error seen (strictly lower replaces) is kept. */
+static void greedy_window(const float* x, int d, int Q, int n_bins, int n_steps,
+                          float* lo_out, float* hi_out, int* bi, int* bj) {
+  float xmin, xmax;
+  row_range(x, d, &xmin, &xmax);
+  *lo_out = xmin;
+  *hi_out = xmax;
+  *bi = 0;
+  *bj = 0;
+  if (xmax == xmin) return;
+  float delta = (xmax - xmin) / (float)n_bins;
+  int i = 0, j = 0;
+  float best = window_sse(x, d, xmin, xmax, Q);
+  int best_i = 0, best_j = 0;
+  for (int step = 0; step < n_steps; ++step) {
+    float lo_next = fmaf((float)(i + 1), delta, xmin) + 0.0f;
+    float lo_cur = fmaf((float)i, delta, xmin) + 0.0f;
+    float hi_cur = fmaf(-(float)j, delta, xmax) + 0.0f;
+    float hi_next = fmaf(-(float)(j + 1), delta, xmax) + 0.0f;
+    float la = window_sse(x, d, lo_next, hi_cur, Q);  /* raise the low end */
+    float lb = window_sse(x, d, lo_cur, hi_next, Q);  /* lower the high end */
+    float l;
+    if (la < lb) {
+      i += 1;
+      l = la;
+    } else {
+      j += 1;
+      l = lb;
+    }
+    if (l < best) {
+      best = l;
+      best_i = i;
+      best_j = j;
+    }
+  }
+  *lo_out = fmaf((float)best_i, delta, xmin) + 0.0f;
+  *hi_out = fmaf(-(float)best_j, delta, xmax) + 0.0f;
+  *bi = best_i;
+  *bj = best_j;
+}
+
+/* Encode one row into its packed form at window [lo, hi]. */
+static void encode_row(const float* x, int d, int bits, float lo, float hi,
+                       uint8_t* row, int64_t stride) {
+  int Q = (1 << bits) - 1;
+  params_t p = make_params(lo, hi, Q);
+  float r = (p.sf == 0.0f) ? 0.0f : 1.0f / p.sf;
+  int64_t C = code_bytes(d, bits);
+  memset(row, 0, (size_t)stride);
+  for (int i = 0; i < d; ++i) {
+    int q = code_of(x[i], p, r, Q);
+    if (bits == 8) {
+      row[i] = (uint8_t)q;
+    } else if ((i & 1) == 0) {
+      row[i / 2] = (uint8_t)(row[i / 2] | q);         /* even element: low nibble */
+    } else {
+      row[i / 2] = (uint8_t)(row[i / 2] | (q << 4));  /* odd element: high nibble */
+    }
+  }
+  row[C + 0] = (uint8_t)(p.s16 & 0xff);
+  row[C + 1] = (uint8_t)(p.s16 >> 8);
+  row[C + 2] = (uint8_t)(p.b16 & 0xff);
+  row[C + 3] = (uint8_t)(p.b16 >> 8);
+}
+
+/* Read back code i and the parameters of a packed row. */
+static int row_code(const uint8_t* row, int i, int bits) {
+  if (bits == 8) return row[i];
+  uint8_t byte = row[i / 2];
+  return (i & 1) ? (byte >> 4) : (byte & 0x0f);
+}
+
+static void row_params(const uint8_t* row, int d, int bits, float* sf, float* bf) {
+  int64_t C = code_bytes(d, bits);
+  uint16_t s16 = (uint16_t)(row[C] | (row[C + 1] << 8));
+  uint16_t b16 = (uint16_t)(row[C + 2] | (row[C + 3] << 8));
+  *sf = from_half(s16);
+  *bf = from_half(b16);
+}
+
+static int row_precondition_ok(const float* x, int d) {
+  for (int i = 0; i < d; ++i) {
+    if (!isfinite(x[i]) || fabsf(x[i]) > 65504.0f) return 0;
+  }
+  return 1;
+}
+
+/* ------------------------------------------------------------------ */
+/* Exported entry points (host pointers)                               */
+/* ------------------------------------------------------------------ */
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* Element-wise binary32 -> binary16 bits, for the conversion check. */
+void oracle_f32_to_f16(const float* in, uint16_t* out, int64_t n) {
+  for (int64_t k = 0; k < n; ++k) out[k] = to_half(in[k]);
+}
+
+void oracle_f16_to_f32(const uint16_t* in, float* out, int64_t n) {
+  for (int64_t k = 0; k < n; ++k) out[k] = from_half(in[k]);
+}
+
+/* clip_mode 0 = row range, 1 = greedy search.  best_ij (nullable) receives
+   the greedy window indices (i, j) per row.  Returns OR_PRECONDITION if any
+   value is non-finite or beyond the binary16 range. */
+int oracle_quantize_rowwise(const float* x, int64_t rows, int dim, int bits,
+                            int clip_mode, int n_bins, int n_steps,
+                            uint8_t* packed, int32_t* best_ij) {
+  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  if (clip_mode != 0 && clip_mode != 1) return OR_INVALID;
+  if (clip_mode == 1 && (n_bins < 1 || n_steps < 0 || n_steps >= n_bins)) return OR_INVALID;
+  int64_t stride = oracle_row_stride(dim, bits);
+  int Q = (1 << bits) - 1;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + r * (int64_t)dim;
+    if (!row_precondition_ok(xr, dim)) {
+      bad = 1;
+      continue;
+    }
+    float lo, hi;
+    int bi = 0, bj = 0;
+    if (clip_mode == 0) {
+      row_range(xr, dim, &lo, &hi);
+    } else {
+      greedy_window(xr, dim, Q, n_bins, n_steps, &lo, &hi, &bi, &bj);
+    }
+    if (best_ij) {
+      best_ij[2 * r] = bi;
+      best_ij[2 * r + 1] = bj;
+    }
+    encode_row(xr, dim, bits, lo, hi, packed + r * stride, stride);
+  }
+  return bad ? OR_PRECONDITION : OR_OK;
+}
+
+/* Squared error of one row at greedy window (i, j), for lattice checks. */
+float oracle_window_sse(const float* x, int dim, int bits, int n_bins, int i, int j) {
+  float xmin, xmax;
+  row_range(x, dim, &xmin, &xmax);
+  float delta = (xmax - xmin) / (float)n_bins;
+  float lo = fmaf((float)i, delta, xmin) + 0.0f;
+  float hi = fmaf(-(float)j, delta, xmax) + 0.0f;
+  return window_sse(x, dim, lo, hi, (1 << bits) - 1);
+}
+
+/* Squared error of a packed row against its source row, in the same order. */
+float oracle_row_sse(const float* x, const uint8_t* row, int dim, int bits) {
+  float u[OR_MAX_DIM];
+  int n = next_pow2(dim);
+  float sf, bf;
+  row_params(row, dim, bits, &sf, &bf);
+  for (int i = 0; i < dim; ++i) {
+    float e = x[i] - dequant_value(sf, bf, row_code(row, i, bits));
+    u[i] = e * e;
+  }
+  for (int i = dim; i < n; ++i) u[i] = 0.0f;
+  return pairwise_sum(u, n);
+}
+
+int oracle_dequantize(const uint8_t* packed, int64_t rows, int dim, int bits, float* y) {
+  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  int64_t stride = oracle_row_stride(dim, bits);
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint8_t* row = packed + r * stride;
+    float sf, bf;
+    row_params(row, dim, bits, &sf, &bf);
+    for (int i = 0; i < dim; ++i) y[r * dim + i] = dequant_value(sf, bf, row_code(row, i, bits));
+  }
+  return OR_OK;
+}
+
+static int64_t load_index(const void* p, int64_t k, int index_type) {
+  return index_type == 0 ? (int64_t)((const int32_t*)p)[k] : ((const int64_t*)p)[k];
+}
+
+/* Pooled lookup over CSR bags.  Bag g = t * B + b covers positions
+   [offsets[g], offsets[g+1]) of indices/weights; its terms are
+   w_p * dequant(row table_offsets[t] + indices[p]), summed in binary64 in
+   position order (w_p = 1 for plain sum).  out is [B][T][dim] (binary64);
+   abs_terms (nullable) gets the sum of |w_p * y| per output element.
+   Invalid data never faults: an index outside the table, or a table whose
+   row range lies outside [0, total_rows), skips that term; a bag whose
+   offsets decrease or leave [0, nnz] is empty.  Each such event adds one to
+   *err_count (nullable). */
+int oracle_bag_forward(const uint8_t* packed, int64_t total_rows,
+                       const int64_t* table_offsets, int T, int64_t B, int dim,
+                       int bits, const void* indices, const void* offsets,
+                       int64_t nnz, int index_type, int pool_mode,
+                       const float* weights, double* out, double* abs_terms,
+                       int64_t* err_count) {
+  if (T < 0 || B < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  if (index_type != 0 && index_type != 1) return OR_INVALID;
+  if (pool_mode != 0 && pool_mode != 1) return OR_INVALID;
+  if (pool_mode == 1 && weights == NULL) return OR_INVALID;
+  int64_t stride = oracle_row_stride(dim, bits);
+  int64_t errors = 0;
+  int64_t G = (int64_t)T * B;
+#pragma omp parallel for schedule(static) reduction(+ : errors)
+  for (int64_t g = 0; g < G; ++g) {
+    int64_t t = g / B, b = g % B;
+    double* o = out + (b * T + t) * (int64_t)dim;
+    double* a = abs_terms ? abs_terms + (b * T + t) * (int64_t)dim : NULL;
+    for (int j = 0; j < dim; ++j) {
+      o[j] = 0.0;
+      if (a) a[j] = 0.0;
+    }
+    int64_t p0 = load_index(offsets, g, index_type);
+    int64_t p1 = load_index(offsets, g + 1, index_type);
+    if (p0 < 0 || p1 < p0 || p1 > nnz) {
+      errors += 1;
+      continue;
+    }
+    int64_t t0 = table_offsets[t], t1 = table_offsets[t + 1];
+    int table_ok = (t0 >= 0 && t1 >= t0 && t1 <= total_rows);
+    for (int64_t p = p0; p < p1; ++p) {
+      int64_t idx = load_index(indices, p, index_type);
+      if (!table_ok || idx < 0 || idx >= t1 - t0) {
+        errors += 1;
+        continue;
+      }
+      const uint8_t* row = packed + (t0 + idx) * stride;
+      float sf, bf;
+      row_params(row, dim, bits, &sf, &bf);
+      double w = pool_mode == 1 ? (double)weights[p] : 1.0;
+      for (int j = 0; j < dim; ++j) {
+        double term = w * (double)dequant_value(sf, bf, row_code(row, j, bits));
+        o[j] += term;
+        if (a) a[j] += fabs(term);
+      }
+    }
+  }
+  if (err_count) *err_count = errors;
+  return OR_OK;
+}
+
+/* Normalized l2 error of a quantized table against its source:
+   out4[0] = mean over rows with ||x|| > 0 of ||x - y|| / ||x||,
+   out4[1] = number of such rows,
+   out4[2] = sum over all rows of ||x - y||^2,
+   out4[3] = sum over all rows of ||x||^2  (binary64 throughout).
+   Rows are summed in fixed blocks of 4096 rows and the blocks in order, so
+   the result does not depend on the thread count. */
+#define OR_L2_BLOCK 4096
+int oracle_l2_error(const float* x, const uint8_t* packed, int64_t rows, int dim,
+                    int bits, double* out4) {
+  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  int64_t stride = oracle_row_stride(dim, bits);
+  int64_t nblk = (rows + OR_L2_BLOCK - 1) / OR_L2_BLOCK;
+  double* part = (double*)calloc((size_t)(nblk > 0 ? nblk : 1) * 4, sizeof(double));
+  if (!part) return OR_INVALID;
+#pragma omp parallel for schedule(static)
+  for (int64_t k = 0; k < nblk; ++k) {
+    double sum_ratio = 0.0, n_rows = 0.0, sum_err = 0.0, sum_x = 0.0;
+    int64_t r_end = (k + 1) * OR_L2_BLOCK < rows ? (k + 1) * OR_L2_BLOCK : rows;
+    for (int64_t r = k * OR_L2_BLOCK; r < r_end; ++r) {
+      const float* xr = x + r * (int64_t)dim;
+      const uint8_t* row = packed + r * stride;
+      float sf, bf;
+      row_params(row, dim, bits, &sf, &bf);
+      double e2 = 0.0, x2 = 0.0;
+      for (int i = 0; i < dim; ++i) {
+        double y = (double)dequant_value(sf, bf, row_code(row, i, bits));
+        double e = (double)xr[i] - y;
+        e2 += e * e;
+        x2 += (double)xr[i] * (double)xr[i];
+      }
+      sum_err += e2;
+      sum_x += x2;
+      if (x2 > 0.0) {
+        sum_ratio += sqrt(e2) / sqrt(x2);
+        n_rows += 1.0;
+      }
+    }
+    part[4 * k + 0] = sum_ratio;
+    part[4 * k + 1] = n_rows;
+    part[4 * k + 2] = sum_err;
+    part[4 * k + 3] = sum_x;
+  }
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int64_t k = 0; k < nblk; ++k)
+    for (int c = 0; c < 4; ++c) acc[c] += part[4 * k + c];
+  free(part);
+  out4[0] = acc[1] > 0.0 ? acc[0] / acc[1] : 0.0;
+  out4[1] = acc[1];
+  out4[2] = acc[2];
+  out4[3] = acc[3];
+  return OR_OK;
+}
