@@ -1,0 +1,184 @@
+/*
+ * qemb.h -- C ABI of libqemb: row-wise INT4/INT8 quantized embedding tables
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Operations (the pages state them in prose; the exact numeric rules are the
+ * project's readings of those passages):
+ *
+ *  - Row-wise uniform quantization: every table row gets its own scale and
+ *    bias, stored as binary16, and 4- or 8-bit codes; the clipping window is
+ *    either the row's range or the result of a greedy search that lowers the
+ *    row's squared error ("Post-Training 4-bit Quantization on Embedding
+ *    Tables", review page, sections "Proposed method" and "Main findings").
+ *  - 4-bit codes are bit-packed two per byte (DQRM repository page, the
+ *    paragraph on the Android demo).
+ *  - Pooled lookup: sparse categorical ids select rows of many embedding
+ *    tables and each bag of ids is reduced to one dense vector ("Deep
+ *    Learning Recommendation Model for Personalization and Recommendation
+ *    Systems", review page, "Proposed method").
+ *  - Normalized l2 quantization error ("Post-Training 4-bit Quantization on
+ *    Embedding Tables", review page, "Proposed method").
+ *
+ * Packed row layout (stride S bytes, S = 16 * ceil((C + 4) / 16),
+ * C = ceil(dim * bits / 8)):
+ *     bytes [0, C)      codes; INT4: element 2k in the low nibble of byte k,
+ *                       element 2k+1 in the high nibble (0 for odd dim);
+ *                       INT8: element k in byte k
+ *     bytes [C, C+2)    scale, binary16, little-endian
+ *     bytes [C+2, C+4)  bias,  binary16, little-endian
+ *     bytes [C+4, S)    zero
+ * Element k of a row decodes to fmaf(scale, (float)code_k, bias).
+ *
+ * Numeric rules of the quantizer (bit-exact; binary32 round-to-nearest-even,
+ * one rounding per operation, no contraction, IEEE division, denormals kept):
+ *     Q = 2^bits - 1
+ *     window [lo, hi]; range mode: lo = min(row) + 0, hi = max(row) + 0
+ *     s = (hi - lo) / Q, replaced by +0 unless s > 0
+ *     s16 = fp16_rne(s), b16 = fp16_rne(lo); sf, bf = their binary32 values
+ *     code_k = 0 if sf == 0, else min(max(rint((x_k - bf) * (1 / sf)), 0), Q)
+ *              with rint rounding half to even
+ *     row error = pairwise sum (contiguous halves, length padded with +0 to a
+ *                 power of two) of (x_k - decoded_k)^2
+ *     greedy mode (n_bins = Bn, n_steps = K, 0 <= K < Bn): from the row's
+ *       range, delta = (max - min) / Bn; window (i, j) is
+ *       lo = fmaf(i, delta, min) + 0, hi = fmaf(-j, delta, max) + 0; starting
+ *       at (0, 0), each of K steps evaluates (i+1, j) and (i, j+1) and moves to
+ *       the one with the smaller error (a tie moves j); the window with the
+ *       smallest error seen (only a strictly smaller error replaces it) is
+ *       encoded.  K = 0 gives the range encoding.
+ * Preconditions: every input value finite with |x| <= 65504; otherwise the
+ * codes of the affected rows are unspecified (no fault).
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller; the
+ *    library allocates nothing, frees nothing, keeps no state between calls
+ *    and never synchronizes.  Work is enqueued on `stream` (NULL = the
+ *    default stream) and errors that can be seen on the host are returned
+ *    synchronously before anything is enqueued.
+ *  - Inputs are read-only; outputs are fully overwritten; inputs and outputs
+ *    must not overlap.
+ *  - Return codes: QEMB_OK, or a negative QEMB_E_* value (qemb_strerror).
+ *  - Calls from several host threads are safe; calls whose outputs overlap
+ *    race.
+ */
+#ifndef QEMB_H
+#define QEMB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* qemb_stream_t; /* the same type as hipStream_t */
+
+#define QEMB_ABI_VERSION 1
+
+#define QEMB_OK 0
+#define QEMB_E_INVALID_ARG -1 /* NULL where required, bad size, mode or type */
+#define QEMB_E_MISALIGNED -2  /* an array is not aligned as documented */
+#define QEMB_E_UNSUPPORTED -3 /* dim above QEMB_MAX_DIM */
+#define QEMB_E_LAUNCH -4      /* the HIP runtime rejected a kernel launch */
+
+#define QEMB_MAX_DIM 1024
+
+#define QEMB_CLIP_RANGE 0
+#define QEMB_CLIP_GREEDY 1
+
+#define QEMB_POOL_SUM 0
+#define QEMB_POOL_WEIGHTED_SUM 1
+
+#define QEMB_INDEX_INT32 0
+#define QEMB_INDEX_INT64 1
+
+/* ABI version of the loaded library (QEMB_ABI_VERSION). */
+int qemb_abi_version(void);
+
+/* Static description of a return code. */
+const char* qemb_strerror(int code);
+
+/* Packed row stride S in bytes for (dim, bits), or -1 if dim < 1,
+ * dim > QEMB_MAX_DIM or bits is not 4 or 8. */
+int64_t qemb_row_stride(int32_t dim, int32_t bits);
+
+/*
+ * Row-wise quantization of an fp32 table (the post-training quantizer of the
+ * "Post-Training 4-bit Quantization on Embedding Tables" review page,
+ * "Proposed method": row-wise uniform quantization, range or greedy clip,
+ * fp16 scale and bias).
+ *   x       [rows][dim] fp32, row-major, 16-byte aligned
+ *   rows    >= 0 (0 = nothing to do)
+ *   dim     1 .. QEMB_MAX_DIM
+ *   bits    4 or 8
+ *   clip_mode  QEMB_CLIP_RANGE or QEMB_CLIP_GREEDY
+ *   n_bins, n_steps  greedy only: 1 <= n_bins, 0 <= n_steps < n_bins
+ *                    (ignored for range mode)
+ *   packed  [rows][S] bytes, 16-byte aligned, written in full
+ */
+int qemb_quantize_rowwise(const float* x, int64_t rows, int32_t dim, int32_t bits,
+                          int32_t clip_mode, int32_t n_bins, int32_t n_steps,
+                          uint8_t* packed, qemb_stream_t stream);
+
+/*
+ * Decode packed rows to fp32: y[r][k] = fmaf(scale_r, code_rk, bias_r)
+ * (same passage as above: fp16 scale and bias per row).
+ *   packed  [rows][S], 16-byte aligned;  y  [rows][dim] fp32, 16-byte aligned
+ */
+int qemb_dequantize(const uint8_t* packed, int64_t rows, int32_t dim, int32_t bits,
+                    float* y, qemb_stream_t stream);
+
+/*
+ * Fused dequantize + pooled embedding-bag lookup over many tables ("Deep
+ * Learning Recommendation Model ..." review page, "Proposed method": sparse
+ * ids are mapped to dense vectors through embedding tables).
+ *   packed         all tables' packed rows back to back, [total_rows][S],
+ *                  16-byte aligned
+ *   total_rows     rows in `packed`
+ *   table_offsets  [T+1] int64, table t owns rows [table_offsets[t],
+ *                  table_offsets[t+1])
+ *   T, B           tables and bags per table (batch); bag g = t * B + b
+ *   indices        [nnz] row ids local to the bag's table (int32 or int64)
+ *   offsets        [T*B + 1] CSR offsets into indices (same type as indices);
+ *                  bag g covers positions [offsets[g], offsets[g+1])
+ *   index_type     QEMB_INDEX_INT32 or QEMB_INDEX_INT64
+ *   pool_mode      QEMB_POOL_SUM (every weight 1) or QEMB_POOL_WEIGHTED_SUM
+ *   weights        [nnz] fp32 per-index weights; required for WEIGHTED_SUM,
+ *                  ignored (may be NULL) for SUM
+ *   out            [B][T][dim] fp32, 16-byte aligned:
+ *                  out[b][t][:] = sum over p in bag g of w_p * decode(row)
+ *                  accumulated in fp32 (any order); an empty bag gives +0
+ *   err_count      nullable int32 counter (device); the caller zeroes it.
+ * Bad device data never faults: a term whose id lies outside its table, or
+ * whose table range leaves [0, total_rows), is skipped; a bag whose offsets
+ * decrease or leave [0, nnz] is empty; each such event adds 1 to *err_count.
+ */
+int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* table_offsets,
+                     int32_t T, int64_t B, int32_t dim, int32_t bits, const void* indices,
+                     const void* offsets, int64_t nnz, int32_t index_type, int32_t pool_mode,
+                     const float* weights, float* out, int32_t* err_count,
+                     qemb_stream_t stream);
+
+/* Bytes of device workspace that qemb_l2_error needs (a fixed size). */
+size_t qemb_l2_error_workspace_bytes(void);
+
+/*
+ * Normalized l2 error of a quantized table against its fp32 source ("Post-
+ * Training 4-bit Quantization on Embedding Tables", review page, "Proposed
+ * method": quantization error measured by a normalized l2 loss), binary64:
+ *   out4[0] = mean over rows with ||x_r|| > 0 of ||x_r - y_r|| / ||x_r||
+ *   out4[1] = number of such rows
+ *   out4[2] = sum over rows of ||x_r - y_r||^2
+ *   out4[3] = sum over rows of ||x_r||^2
+ * x [rows][dim] fp32 and packed [rows][S], both 16-byte aligned; workspace
+ * of qemb_l2_error_workspace_bytes() bytes, 16-byte aligned; out4 double[4]
+ * (device).  The reduction order is fixed, so results repeat exactly.
+ */
+int qemb_l2_error(const float* x, const uint8_t* packed, int64_t rows, int32_t dim,
+                  int32_t bits, void* workspace, double* out4, qemb_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QEMB_H */

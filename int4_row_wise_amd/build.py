@@ -1,0 +1,62 @@
+"""Build libqemb.so (the HIP C-ABI library) in-tree for gfx950.
+
+    python -m int4_row_wise_amd.build
+
+hipcc cross-compiles on a machine without a GPU.  Flags: no fast-math and no
+floating-point contraction (the quantizer must round exactly as its rules
+say), packed-fp32 instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "qemb.hip")
+HEADER = os.path.join(ROOT, "include", "qemb.h")
+LIB = os.path.join(HERE, "libqemb.so")
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fPIC", "-shared", "-Wall",
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", "hipcc"):
+        if c and (os.path.isabs(c) and os.path.exists(c) or not os.path.isabs(c)):
+            return c
+    return "hipcc"
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile csrc/qemb.hip into int4_row_wise_amd/libqemb.so."""
+    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(
+            os.path.getmtime(SRC), os.path.getmtime(HEADER)):
+        return LIB
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + out)
+    if out.strip() and verbose:
+        print(out)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def ensure_built() -> str:
+    """Build only if no library exists yet (used by tests, smoke and bench)."""
+    if os.path.exists(LIB):
+        return LIB
+    return build(force=True)
+
+
+if __name__ == "__main__":
+    print(build(force=True, verbose="-v" in sys.argv))

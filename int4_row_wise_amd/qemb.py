@@ -1,0 +1,195 @@
+"""Thin ctypes binding over libqemb.so (include/qemb.h).
+
+Argument marshalling only: every step of quantization, decoding, pooling and
+the error measurement runs in the HIP kernels behind the C ABI.  torch is
+used for device memory (output allocation) and the current stream.  The
+library is loaded on first use; if it was not built this raises -- there is
+no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqemb.so")
+
+RANGE, GREEDY = 0, 1
+SUM, WEIGHTED_SUM = 0, 1
+INDEX_INT32, INDEX_INT64 = 0, 1
+MAX_DIM = 1024
+
+EXPORTED = (
+    "qemb_abi_version", "qemb_strerror", "qemb_row_stride", "qemb_quantize_rowwise",
+    "qemb_dequantize", "qemb_bag_forward", "qemb_l2_error_workspace_bytes", "qemb_l2_error",
+)
+
+
+class QembError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__("%s failed: %s (%d)" % (fn, msg, code))
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise QembError("load_library", -100,
+                        "%s is not built (run `python -m int4_row_wise_amd.build`)" % path)
+    L = ctypes.CDLL(path)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.qemb_abi_version.restype = ctypes.c_int
+    L.qemb_strerror.argtypes = [ctypes.c_int]
+    L.qemb_strerror.restype = ctypes.c_char_p
+    L.qemb_row_stride.argtypes = [i32, i32]
+    L.qemb_row_stride.restype = i64
+    L.qemb_quantize_rowwise.argtypes = [p, i64, i32, i32, i32, i32, i32, p, p]
+    L.qemb_quantize_rowwise.restype = ctypes.c_int
+    L.qemb_dequantize.argtypes = [p, i64, i32, i32, p, p]
+    L.qemb_dequantize.restype = ctypes.c_int
+    L.qemb_bag_forward.argtypes = [p, i64, p, i32, i64, i32, i32, p, p, i64, i32, i32, p, p, p, p]
+    L.qemb_bag_forward.restype = ctypes.c_int
+    L.qemb_l2_error_workspace_bytes.restype = ctypes.c_size_t
+    L.qemb_l2_error.argtypes = [p, p, i64, i32, i32, p, p, p]
+    L.qemb_l2_error.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise QembError(fn, rc, load_library().qemb_strerror(rc).decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(name: str, t: torch.Tensor, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a CUDA (HIP) tensor" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def abi_version() -> int:
+    return int(load_library().qemb_abi_version())
+
+
+def row_stride(dim: int, bits: int) -> int:
+    s = int(load_library().qemb_row_stride(dim, bits))
+    if s < 0:
+        raise ValueError("unsupported dim=%d bits=%d" % (dim, bits))
+    return s
+
+
+def _clip(mode) -> int:
+    if isinstance(mode, str):
+        return {"range": RANGE, "greedy": GREEDY}[mode]
+    return int(mode)
+
+
+def quantize_rowwise(x: torch.Tensor, bits: int = 4, clip_mode=RANGE, n_bins: int = 200,
+                     n_steps: int = 100, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [rows, dim] float32 (device) -> packed [rows, stride] uint8."""
+    _dev("x", x, torch.float32)
+    rows, dim = x.shape
+    S = row_stride(dim, bits)
+    if out is None:
+        out = torch.empty((rows, S), dtype=torch.uint8, device=x.device)
+    _dev("out", out, torch.uint8)
+    if tuple(out.shape) != (rows, S):
+        raise ValueError("out must be [%d, %d]" % (rows, S))
+    _check("qemb_quantize_rowwise", load_library().qemb_quantize_rowwise(
+        _ptr(x), rows, dim, bits, _clip(clip_mode), n_bins, n_steps, _ptr(out), _stream(x)))
+    return out
+
+
+def dequantize(packed: torch.Tensor, dim: int, bits: int = 4,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """packed [rows, stride] uint8 (device) -> [rows, dim] float32."""
+    _dev("packed", packed, torch.uint8)
+    rows = packed.shape[0]
+    if packed.dim() != 2 or packed.shape[1] != row_stride(dim, bits):
+        raise ValueError("packed must be [rows, %d]" % row_stride(dim, bits))
+    if out is None:
+        out = torch.empty((rows, dim), dtype=torch.float32, device=packed.device)
+    _dev("out", out, torch.float32)
+    _check("qemb_dequantize", load_library().qemb_dequantize(
+        _ptr(packed), rows, dim, bits, _ptr(out), _stream(packed)))
+    return out
+
+
+def bag_forward(packed: torch.Tensor, table_offsets: torch.Tensor, B: int, dim: int, bits: int,
+                indices: torch.Tensor, offsets: torch.Tensor, weights: Optional[torch.Tensor] = None,
+                pool_mode: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                err_count: Optional[torch.Tensor] = None,
+                total_rows: Optional[int] = None) -> torch.Tensor:
+    """Pooled lookup: out [B, T, dim] float32; bag g = t*B + b spans
+    indices[offsets[g]:offsets[g+1]] (ids local to table t)."""
+    _dev("packed", packed, torch.uint8)
+    _dev("table_offsets", table_offsets, torch.int64)
+    _dev("indices", indices)
+    _dev("offsets", offsets, indices.dtype)
+    if indices.dtype == torch.int32:
+        itype = INDEX_INT32
+    elif indices.dtype == torch.int64:
+        itype = INDEX_INT64
+    else:
+        raise TypeError("indices must be int32 or int64")
+    T = table_offsets.numel() - 1
+    if offsets.numel() != T * B + 1:
+        raise ValueError("offsets must have T*B+1 = %d entries" % (T * B + 1))
+    if pool_mode is None:
+        pool_mode = SUM if weights is None else WEIGHTED_SUM
+    if weights is not None:
+        _dev("weights", weights, torch.float32)
+        if weights.numel() != indices.numel():
+            raise ValueError("weights must match indices")
+    if out is None:
+        out = torch.empty((B, T, dim), dtype=torch.float32, device=packed.device)
+    _dev("out", out, torch.float32)
+    if err_count is not None:
+        _dev("err_count", err_count, torch.int32)
+    if total_rows is None:
+        total_rows = packed.shape[0]
+    _check("qemb_bag_forward", load_library().qemb_bag_forward(
+        _ptr(packed), total_rows, _ptr(table_offsets), T, B, dim, bits, _ptr(indices),
+        _ptr(offsets), indices.numel(), itype, pool_mode, _ptr(weights), _ptr(out),
+        _ptr(err_count), _stream(packed)))
+    return out
+
+
+def l2_error_workspace_bytes() -> int:
+    return int(load_library().qemb_l2_error_workspace_bytes())
+
+
+def l2_error(x: torch.Tensor, packed: torch.Tensor, bits: int,
+             workspace: Optional[torch.Tensor] = None, out4: Optional[torch.Tensor] = None) -> dict:
+    """Normalized l2 error of packed rows against x (binary64, on the device)."""
+    _dev("x", x, torch.float32)
+    _dev("packed", packed, torch.uint8)
+    rows, dim = x.shape
+    if workspace is None:
+        workspace = torch.empty(l2_error_workspace_bytes(), dtype=torch.uint8, device=x.device)
+    if out4 is None:
+        out4 = torch.empty(4, dtype=torch.float64, device=x.device)
+    _check("qemb_l2_error", load_library().qemb_l2_error(
+        _ptr(x), _ptr(packed), rows, dim, bits, _ptr(workspace), _ptr(out4), _stream(x)))
+    v = out4.cpu().tolist()
+    frob = (v[2] / v[3]) ** 0.5 if v[3] > 0 else 0.0
+    return {"mean_row": v[0], "rows": int(v[1]), "sum_err2": v[2], "sum_x2": v[3], "frobenius": frob}

@@ -1,0 +1,116 @@
+"""The C-ABI library loads, exports every entry point include/qemb.h
+declares, and rejects bad arguments on the host before touching the GPU
+(no compute call here)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from int4_row_wise_amd import build as qbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    qbuild.ensure_built()
+    from int4_row_wise_amd import qemb
+    return qemb.load_library()
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "qemb.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qemb_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    syms = declared_symbols()
+    assert len(syms) >= 8
+    for s in syms:
+        assert hasattr(lib, s), s
+    from int4_row_wise_amd import qemb
+    assert sorted(qemb.EXPORTED) == syms
+
+
+def test_abi_version_and_strerror(lib):
+    assert lib.qemb_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -99):
+        assert isinstance(lib.qemb_strerror(code), bytes)
+
+
+def test_row_stride_matches_oracle(lib):
+    for bits in (4, 8):
+        for dim in range(1, 1025):
+            assert lib.qemb_row_stride(dim, bits) == oracle.row_stride(dim, bits)
+    assert lib.qemb_row_stride(0, 4) == -1
+    assert lib.qemb_row_stride(1025, 4) == -1
+    assert lib.qemb_row_stride(16, 5) == -1
+
+
+FAKE = ctypes.c_void_p(1 << 20)       # never dereferenced: validation fails first
+MIS = ctypes.c_void_p((1 << 20) + 4)  # not 16-byte aligned
+
+
+def test_quantize_argument_errors(lib):
+    q = lib.qemb_quantize_rowwise
+    assert q(FAKE, 10, 16, 5, 0, 200, 100, FAKE, None) == -1          # bits
+    assert q(FAKE, 10, 0, 4, 0, 200, 100, FAKE, None) == -1           # dim
+    assert q(FAKE, -1, 16, 4, 0, 200, 100, FAKE, None) == -1          # rows
+    assert q(FAKE, 10, 16, 4, 2, 200, 100, FAKE, None) == -1          # clip mode
+    assert q(FAKE, 10, 16, 4, 1, 100, 100, FAKE, None) == -1          # n_steps >= n_bins
+    assert q(FAKE, 10, 16, 4, 1, 0, 0, FAKE, None) == -1              # n_bins < 1
+    assert q(FAKE, 10, 1025, 4, 0, 200, 100, FAKE, None) == -3        # dim > max
+    assert q(None, 10, 16, 4, 0, 200, 100, FAKE, None) == -1          # NULL x
+    assert q(MIS, 10, 16, 4, 0, 200, 100, FAKE, None) == -2           # misaligned x
+    assert q(FAKE, 10, 16, 4, 0, 200, 100, MIS, None) == -2           # misaligned out
+    assert q(None, 0, 16, 4, 0, 200, 100, None, None) == 0            # nothing to do
+
+
+def test_dequantize_argument_errors(lib):
+    d = lib.qemb_dequantize
+    assert d(FAKE, 10, 16, 3, FAKE, None) == -1
+    assert d(None, 10, 16, 4, FAKE, None) == -1
+    assert d(FAKE, 10, 16, 4, MIS, None) == -2
+    assert d(FAKE, 10, 2000, 4, FAKE, None) == -3
+    assert d(None, 0, 16, 4, None, None) == 0
+
+
+def test_bag_argument_errors(lib):
+    b = lib.qemb_bag_forward
+    #          packed rows toff T  B  dim bits idx  offs nnz itype pool  w     out   err  stream
+    assert b(FAKE, 10, FAKE, 2, 4, 16, 4, FAKE, FAKE, 5, 2, 0, None, FAKE, None, None) == -1
+    assert b(FAKE, 10, FAKE, 2, 4, 16, 4, FAKE, FAKE, 5, 0, 2, None, FAKE, None, None) == -1
+    assert b(FAKE, 10, FAKE, 2, 4, 16, 4, FAKE, FAKE, 5, 0, 1, None, FAKE, None, None) == -1
+    assert b(FAKE, 10, FAKE, 2, 4, 16, 4, None, FAKE, 5, 0, 0, None, FAKE, None, None) == -1
+    assert b(FAKE, 10, None, 2, 4, 16, 4, FAKE, FAKE, 5, 0, 0, None, FAKE, None, None) == -1
+    assert b(FAKE, 10, FAKE, 2, 4, 16, 4, FAKE, FAKE, 5, 0, 0, None, MIS, None, None) == -2
+    assert b(MIS, 10, FAKE, 2, 4, 16, 4, FAKE, FAKE, 5, 0, 0, None, FAKE, None, None) == -2
+    assert b(FAKE, 10, FAKE, 2, 4, 4096, 4, FAKE, FAKE, 5, 0, 0, None, FAKE, None, None) == -3
+    assert b(FAKE, -1, FAKE, 2, 4, 16, 4, FAKE, FAKE, 5, 0, 0, None, FAKE, None, None) == -1
+    assert b(None, 0, None, 0, 4, 16, 4, None, None, 0, 0, 0, None, None, None, None) == 0
+    assert b(None, 0, None, 3, 0, 16, 4, None, None, 0, 0, 0, None, None, None, None) == 0
+
+
+def test_l2_argument_errors(lib):
+    e = lib.qemb_l2_error
+    assert lib.qemb_l2_error_workspace_bytes() > 0
+    assert e(FAKE, FAKE, 10, 16, 4, None, FAKE, None) == -1
+    assert e(FAKE, FAKE, 10, 16, 4, MIS, FAKE, None) == -2
+    assert e(FAKE, FAKE, 10, 16, 7, FAKE, FAKE, None) == -1
+
+
+def test_binding_has_no_cpu_fallback(tmp_path):
+    from int4_row_wise_amd import qemb
+    saved = qemb._lib
+    try:
+        qemb._lib = None
+        with pytest.raises(qemb.QembError):
+            qemb.load_library(str(tmp_path / "missing.so"))
+    finally:
+        qemb._lib = saved
