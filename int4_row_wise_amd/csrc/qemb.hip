@@ -5,7 +5,9 @@
 //   * quantize_greedy_kernel  greedy clip search on the row's squared error,
 //                             then the same encoding
 //   * dequant_kernel          packed rows -> fp32
-//   * bag_kernel              fused decode + (weighted) sum pooling over CSR bags
+//   * bag_wave_kernel         fused decode + (weighted) sum pooling, one wave per
+//                             multi-hot bag
+//   * bag_slice_kernel        the same for short bags, several bags per wave
 //   * l2_partial/l2_final     normalized l2 error, fixed-order reduction
 //
 // The method: row-wise uniform quantization with fp16 scale and bias, clip
@@ -82,12 +84,15 @@ __device__ __forceinline__ uint32_t param_part(uint32_t p32, int off) {
   return off >= 0 ? (p32 << (8 * off)) : (p32 >> (-8 * off));
 }
 
-// Load the 4 parameter bytes at byte C of a 16-byte aligned row.
-__device__ __forceinline__ uint32_t load_params(const uint8_t* row, int C) {
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(row + (C & ~3));
-  const int sh = C & 3;
-  if (sh == 0) return p[0];
-  return __builtin_amdgcn_alignbyte(p[1], p[0], (uint32_t)sh);
+// Load the 4 parameter bytes at byte C of a 16-byte aligned row of stride S
+// bytes.  Both dwords are loaded unconditionally (the second address is
+// clamped inside the row; alignbyte by 0 keeps the first), so no branch sits
+// between a load and its use and the loads of many rows stay in flight.
+__device__ __forceinline__ uint32_t load_params(const uint8_t* row, int C, int S) {
+  const int c4 = C & ~3;
+  const uint32_t lo = *reinterpret_cast<const uint32_t*>(row + c4);
+  const uint32_t hi = *reinterpret_cast<const uint32_t*>(row + (c4 + 4 < S ? c4 + 4 : S - 4));
+  return __builtin_amdgcn_alignbyte(hi, lo, (uint32_t)(C & 3));
 }
 
 template <int N>
@@ -104,9 +109,46 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ int64_t load_index(const void* p, int64_t k, int idx64) {
-  return idx64 ? reinterpret_cast<const int64_t*>(p)[k]
-               : (int64_t)reinterpret_cast<const int32_t*>(p)[k];
+template <typename IdxT>
+__device__ __forceinline__ int64_t load_index(const void* p, int64_t k) {
+  return (int64_t) reinterpret_cast<const IdxT*>(p)[k];
+}
+
+// ---------------------------------------------------------------------------
+// decode + accumulate.  A code placed in the low bits of a binary16 half is
+// the denormal code * 2^-24, so v_fma_mix_f32(scale * 2^24, half, bias) is
+// fmaf(scale, code, bias) with the same single rounding and no int->float
+// conversion; unpacking 8 nibbles into such halves takes 7 ALU ops.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float h16(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu));
+}
+
+// sfs = scale * 2^24 (exact), bf = bias; y_k = fmaf(scale, code_k, bias)
+template <int BITS>
+__device__ __forceinline__ void decode_dword(uint32_t wd, float sfs, float bf, float (&y)[32 / BITS]) {
+  if (BITS == 4) {
+    const uint32_t r04 = wd & 0x000f000fu;
+    const uint32_t r15 = (wd >> 4) & 0x000f000fu;
+    const uint32_t r26 = (wd >> 8) & 0x000f000fu;
+    const uint32_t r37 = (wd >> 12) & 0x000f000fu;
+    y[0] = __builtin_fmaf(sfs, h16(r04), bf);
+    y[1] = __builtin_fmaf(sfs, h16(r15), bf);
+    y[2] = __builtin_fmaf(sfs, h16(r26), bf);
+    y[3] = __builtin_fmaf(sfs, h16(r37), bf);
+    y[4] = __builtin_fmaf(sfs, h16(r04 >> 16), bf);
+    y[5] = __builtin_fmaf(sfs, h16(r15 >> 16), bf);
+    y[6] = __builtin_fmaf(sfs, h16(r26 >> 16), bf);
+    y[7] = __builtin_fmaf(sfs, h16(r37 >> 16), bf);
+  } else {
+    const uint32_t r02 = wd & 0x00ff00ffu;
+    const uint32_t r13 = (wd >> 8) & 0x00ff00ffu;
+    y[0] = __builtin_fmaf(sfs, h16(r02), bf);
+    y[1] = __builtin_fmaf(sfs, h16(r13), bf);
+    y[2] = __builtin_fmaf(sfs, h16(r02 >> 16), bf);
+    y[3] = __builtin_fmaf(sfs, h16(r13 >> 16), bf);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -343,8 +385,8 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(const uint8_t* __restri
   for (int64_t row = (int64_t)blockIdx.x * (kBlock / LPR) + threadIdx.x / LPR; row < rows;
        row += groups) {
     const uint8_t* prow = packed + row * (int64_t)S;
-    const uint32_t p = load_params(prow, C);
-    const float sf = half_value(p), bf = half_value(p >> 16);
+    const uint32_t p = load_params(prow, C, S);
+    const float sfs = half_value(p) * 16777216.0f, bf = half_value(p >> 16);
     float* yr = y + row * dim;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -352,15 +394,19 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(const uint8_t* __restri
       if (e0 >= dim) break;
       float o[EPL];
       if (BITS == 4) {
-        const uint32_t wd = *reinterpret_cast<const uint32_t*>(prow + e0 / 2);
+        float yk[8];
+        decode_dword<4>(*reinterpret_cast<const uint32_t*>(prow + e0 / 2), sfs, bf, yk);
 #pragma unroll
-        for (int k = 0; k < EPL; ++k) o[k] = __builtin_fmaf(sf, (float)((wd >> (4 * k)) & 15u), bf);
+        for (int k = 0; k < 8; ++k) o[k] = yk[k];
       } else {
         const uint2 wd = *reinterpret_cast<const uint2*>(prow + e0);
+        float y0[4], y1[4];
+        decode_dword<8>(wd.x, sfs, bf, y0);
+        decode_dword<8>(wd.y, sfs, bf, y1);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          o[k] = __builtin_fmaf(sf, (float)((wd.x >> (8 * k)) & 255u), bf);
-          o[k + 4] = __builtin_fmaf(sf, (float)((wd.y >> (8 * k)) & 255u), bf);
+          o[k] = y0[k];
+          o[k + 4] = y1[k];
         }
       }
       if (vec4 && e0 + EPL <= dim) {
@@ -376,11 +422,12 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(const uint8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// pooled lookup.  A bag is owned by a slice of LPR*RG lanes: RG row groups of
-// LPR lanes; lane (g, s) reads VEC code bytes at byte s*VEC of rows
-// p0+g, p0+g+RG, ...  U rows per group are in flight per iteration (all their
-// loads are issued before any is used).  The RG partial vectors are reduced
-// across the slice by xor shuffles.
+// pooled lookup
+//
+// acc[k] += w * fmaf(sf, code_k, bf): each term is the decoded value (one
+// rounding, as a standalone decode gives) times the weight, so the fp32
+// accumulation error stays relative to sum |w * y| even when the bias is much
+// larger than the decoded values.
 // ---------------------------------------------------------------------------
 
 template <int BITS, int VEC>
@@ -402,41 +449,31 @@ struct CodeChunk<BITS, 16> {
   }
 };
 
-// acc[k] += w * fmaf(sf, code_k, bf): each term is the decoded value (one
-// rounding, as a standalone decode gives) times the weight, so the fp32
-// accumulation error stays relative to sum |w * y| even when the bias is much
-// larger than the decoded values.
-template <int BITS, int VEC>
+template <int BITS, int VEC, bool INIT = false>
 __device__ __forceinline__ void accumulate(float* acc, const CodeChunk<BITS, VEC>& c, float w,
-                                           float sf, float bf) {
+                                           uint32_t prm) {
+  constexpr int PER = 32 / BITS;  // elements per dword
+  const float sfs = h16(prm) * 16777216.0f;
+  const float bf = h16(prm >> 16);
 #pragma unroll
   for (int d = 0; d < VEC / 4; ++d) {
-    const uint32_t wd = c.dw(d);
-    if (BITS == 4) {
-      const uint32_t lo = wd & 0x0f0f0f0fu;         // elements 0, 2, 4, 6 of this dword
-      const uint32_t hi = (wd >> 4) & 0x0f0f0f0fu;  // elements 1, 3, 5, 7
+    float y[PER];
+    decode_dword<BITS>(c.dw(d), sfs, bf, y);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float y0 = __builtin_fmaf(sf, (float)((lo >> (8 * b)) & 255u), bf);
-        const float y1 = __builtin_fmaf(sf, (float)((hi >> (8 * b)) & 255u), bf);
-        acc[8 * d + 2 * b] = __builtin_fmaf(w, y0, acc[8 * d + 2 * b]);
-        acc[8 * d + 2 * b + 1] = __builtin_fmaf(w, y1, acc[8 * d + 2 * b + 1]);
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float y = __builtin_fmaf(sf, (float)((wd >> (8 * b)) & 255u), bf);
-        acc[4 * d + b] = __builtin_fmaf(w, y, acc[4 * d + b]);
-      }
-    }
+    for (int k = 0; k < PER; ++k)
+      acc[PER * d + k] = INIT ? w * y[k] : __builtin_fmaf(w, y[k], acc[PER * d + k]);
   }
 }
 
-template <int BITS, int VEC, int LPR, int RG, int U>
-__global__ __launch_bounds__(kBlock) void bag_kernel(
+// Short bags (few ids per bag): a bag is owned by a slice of LPR*RG lanes,
+// RG row groups of LPR lanes; lane (g, s) reads VEC code bytes at byte s*VEC
+// of rows p0+g, p0+g+RG, ...  U rows per group are in flight per iteration.
+// The RG partial vectors are reduced across the slice by xor shuffles.
+template <int BITS, int VEC, int LPR, int RG, int U, typename IdxT>
+__global__ __launch_bounds__(kBlock) void bag_slice_kernel(
     const uint8_t* __restrict__ packed, int64_t S, int64_t total_rows,
     const int64_t* __restrict__ table_offsets, int T, int64_t B, int dim, int C,
-    const void* __restrict__ indices, const void* __restrict__ offsets, int idx64, int64_t nnz,
+    const void* __restrict__ indices, const void* __restrict__ offsets, int64_t nnz,
     const float* __restrict__ weights, float* __restrict__ out, int32_t* __restrict__ err_count,
     int64_t n_bags, int vec4) {
   constexpr int EPL = VEC * 8 / BITS;
@@ -450,8 +487,8 @@ __global__ __launch_bounds__(kBlock) void bag_kernel(
   const int64_t t = bag / B;
   const int64_t b = bag - t * B;
   int errs = 0;
-  int64_t p0 = load_index(offsets, bag, idx64);
-  int64_t p1 = load_index(offsets, bag + 1, idx64);
+  int64_t p0 = load_index<IdxT>(offsets, bag);
+  int64_t p1 = load_index<IdxT>(offsets, bag + 1);
   if (!(p0 >= 0 && p1 >= p0 && p1 <= nnz)) {
     errs += (sl == 0);
     p0 = p1 = 0;
@@ -460,8 +497,7 @@ __global__ __launch_bounds__(kBlock) void bag_kernel(
   const bool table_ok = t0 >= 0 && t1 >= t0 && t1 <= total_rows;
   const int64_t n_t = table_ok ? t1 - t0 : 0;
   const bool has_codes = s * VEC < C;
-  const uint8_t* tbase = packed + (table_ok ? t0 : 0) * S + s * VEC;
-  const uint8_t* pbase = packed + (table_ok ? t0 : 0) * S;
+  const uint8_t* tbase = packed + (table_ok ? t0 : 0) * S;
 
   float acc[EPL];
 #pragma unroll
@@ -475,26 +511,25 @@ __global__ __launch_bounds__(kBlock) void bag_kernel(
     for (int u = 0; u < U; ++u) {
       const int64_t p = base + u * RG + g;
       const bool in = p < p1;
-      id[u] = in ? load_index(indices, p, idx64) : 0;
-      w[u] = in ? (weights ? weights[p] : 1.0f) : 0.0f;
+      id[u] = in ? load_index<IdxT>(indices, p) : 0;
       ok[u] = in && id[u] >= 0 && id[u] < n_t;
+      w[u] = ok[u] ? (weights ? weights[p] : 1.0f) : 0.0f;
       errs += (in && !ok[u] && s == 0);
     }
     CodeChunk<BITS, VEC> cc[U];
     uint32_t pr[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const uint8_t* row = tbase + id[u] * S;
       if (ok[u] && has_codes) {
-        cc[u].load(tbase + id[u] * S);
+        cc[u].load(row + s * VEC);
       } else {
         cc[u].zero();
       }
-      pr[u] = ok[u] ? load_params(pbase + id[u] * S, C) : 0u;
+      pr[u] = ok[u] ? load_params(row, C, (int)S) : 0u;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      accumulate<BITS, VEC>(acc, cc[u], w[u], half_value(pr[u]), half_value(pr[u] >> 16));
-    }
+    for (int u = 0; u < U; ++u) accumulate<BITS, VEC>(acc, cc[u], w[u], pr[u]);
   }
 
 #pragma unroll
@@ -515,6 +550,554 @@ __global__ __launch_bounds__(kBlock) void bag_kernel(
       for (int k = 0; k < EPL; ++k)
         if (e0 + k < dim) o[e0 + k] = acc[k];
     }
+  }
+  if (errs && err_count) atomicAdd(err_count, errs);
+}
+
+// Multi-hot bags: each wave walks kWave consecutive bags.  Lane i holds the
+// CSR bounds of bag i of the run; for the current bag, lane L validates id L
+// (64 ids at a time) once and leaves its row offset and weight in LDS, while
+// the ids of the next bag are already being fetched.  The 64 lanes form
+// RG = 64/LPR row groups of LPR lanes (LPR*VEC code bytes cover a row); group
+// g takes rows g, g+RG, ... of the batch, with all of them (up to UMAX per
+// group) in flight at once and the batch sized to the rows left.  Each lane
+// accumulates EPL = 16 elements; the RG partial vectors are summed through
+// LDS in a fixed order and written with coalesced stores.  Consecutive blocks
+// go round-robin over the 8 XCDs, so block ids are remapped to give each XCD
+// a contiguous run of bags (a few tables): each XCD's L2 then holds fewer
+// tables' hot rows.
+constexpr int kWPB = kBlock / kWave;
+constexpr int kBagUMax = 8;
+
+template <int BITS, int LPR>
+struct WaveBag {
+  static constexpr int VEC = 2 * BITS;  // bytes per lane per row: 16 codes
+  static constexpr int EPL = VEC * 8 / BITS;
+  static constexpr int RG = kWave / LPR;
+};
+
+// Rows j0 + u*RG + g (u < U) of the current id batch.  Every lane loads
+// unconditionally: a slot without a valid row reads the table's first row
+// (`safe`) at byte 0 and gets zero scale and bias, so it adds exactly 0; a
+// lane whose chunk lies past the row's code bytes also reads at byte 0 (its
+// elements are never stored).
+template <int BITS, int LPR, int U>
+__device__ __forceinline__ void wave_bag_rows(float* acc, const uint8_t* safe, int C, int S, int code_off,
+                                              int g, int j0, int n, const int64_t* moff,
+                                              const float* mw) {
+  using W = WaveBag<BITS, LPR>;
+  int64_t off[U];
+  float w[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int slot = j0 + u * W::RG + g;
+    off[u] = slot < n ? moff[slot] : -1;
+    w[u] = slot < n ? mw[slot] : 0.0f;
+  }
+  CodeChunk<BITS, W::VEC> cc[U];
+  uint32_t pr[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint8_t* row = safe + (off[u] >= 0 ? off[u] : 0);
+    cc[u].load(row + (off[u] >= 0 ? code_off : 0));
+    pr[u] = load_params(row, C, (int)S);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    accumulate<BITS, W::VEC>(acc, cc[u], w[u], off[u] >= 0 ? pr[u] : 0u);
+}
+
+template <int BITS, int LPR>
+__device__ __forceinline__ void wave_bag_batch(float* acc, const uint8_t* safe, int C, int S, int code_off,
+                                               int g, int n, const int64_t* moff, const float* mw) {
+  constexpr int RG = WaveBag<BITS, LPR>::RG;
+  for (int j0 = 0; j0 < n; j0 += kBagUMax * RG) {
+    const int u = (n - j0 + RG - 1) / RG;
+    switch (u < kBagUMax ? u : kBagUMax) {
+      case 1: wave_bag_rows<BITS, LPR, 1>(acc, safe, C, S, code_off, g, j0, n, moff, mw); break;
+      case 2: wave_bag_rows<BITS, LPR, 2>(acc, safe, C, S, code_off, g, j0, n, moff, mw); break;
+      case 3: wave_bag_rows<BITS, LPR, 3>(acc, safe, C, S, code_off, g, j0, n, moff, mw); break;
+      case 4: wave_bag_rows<BITS, LPR, 4>(acc, safe, C, S, code_off, g, j0, n, moff, mw); break;
+      case 5: wave_bag_rows<BITS, LPR, 5>(acc, safe, C, S, code_off, g, j0, n, moff, mw); break;
+      case 6: wave_bag_rows<BITS, LPR, 6>(acc, safe, C, S, code_off, g, j0, n, moff, mw); break;
+      case 7: wave_bag_rows<BITS, LPR, 7>(acc, safe, C, S, code_off, g, j0, n, moff, mw); break;
+      default: wave_bag_rows<BITS, LPR, 8>(acc, safe, C, S, code_off, g, j0, n, moff, mw); break;
+    }
+  }
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int64_t lane_i64(int64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), lane);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <int BITS, int LPR, typename IdxT>
+__global__ __launch_bounds__(kBlock) void bag_wave_kernel(
+    const uint8_t* __restrict__ packed, int64_t S, int64_t total_rows,
+    const int64_t* __restrict__ table_offsets, int T, int64_t B, int dim, int C,
+    const void* __restrict__ indices, const void* __restrict__ offsets, int64_t nnz,
+    const float* __restrict__ weights, float* __restrict__ out, int32_t* __restrict__ err_count,
+    int64_t n_bags) {
+  using W = WaveBag<BITS, LPR>;
+  constexpr int EPL = W::EPL, RG = W::RG;
+  __shared__ int64_t meta_off[kWPB][kWave];
+  __shared__ float meta_w[kWPB][kWave];
+  __shared__ float red[RG > 1 ? kWPB : 1][RG > 1 ? kWave * EPL : 1];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / LPR, s = lane % LPR;
+  // XCD-aware block order (a bijection on [0, gridDim.x))
+  const int64_t nbk = gridDim.x, x = blockIdx.x % 8, k = blockIdx.x / 8;
+  const int64_t qf = nbk / 8, r = nbk % 8;
+  const int64_t blk = x * qf + (x < r ? x : r) + k;
+  const int64_t bag0 = (blk * kWPB + wv) * kWave;
+  if (bag0 >= n_bags) return;  // whole waves leave together
+  const int nb = (int)((n_bags - bag0) < kWave ? (n_bags - bag0) : kWave);
+  int errs = 0;
+
+  // CSR bounds of the run's bags, one bag per lane; bad bounds -> empty bag
+  int64_t lp0 = 0, lp1 = 0;
+  if (lane < nb) {
+    lp0 = load_index<IdxT>(offsets, bag0 + lane);
+    lp1 = load_index<IdxT>(offsets, bag0 + lane + 1);
+    if (!(lp0 >= 0 && lp1 >= lp0 && lp1 <= nnz)) {
+      errs += 1;
+      lp0 = lp1 = 0;
+    }
+  }
+  const int code_off = s * W::VEC < C ? s * W::VEC : 0;
+  int64_t* moff = meta_off[wv];
+  float* mw = meta_w[wv];
+
+  // table of the current bag (bags are table-major)
+  int64_t t = bag0 / B;
+  int64_t t_end = (t + 1) * B;  // first bag of the next table
+  int64_t t0 = 0, n_t = 0;
+  const uint8_t* tbase = packed;
+  auto enter_table = [&](int64_t tt) {
+    const int64_t a0 = table_offsets[tt], a1 = table_offsets[tt + 1];
+    const bool ok = a0 >= 0 && a1 >= a0 && a1 <= total_rows;
+    t0 = ok ? a0 : 0;
+    n_t = ok ? a1 - a0 : 0;
+    tbase = packed + t0 * S;
+  };
+  enter_table(t);
+
+  // first id batch of bag 0
+  int64_t p0 = lane_i64(lp0, 0), p1 = lane_i64(lp1, 0);
+  int64_t nid = 0;
+  float nw = 0.0f;
+  if (lane < p1 - p0) {
+    nid = load_index<IdxT>(indices, p0 + lane);
+    nw = weights ? weights[p0 + lane] : 1.0f;
+  }
+
+  for (int i = 0; i < nb; ++i) {
+    const int64_t bag = bag0 + i;
+    if (bag >= t_end) {
+      t = bag / B;
+      t_end = (t + 1) * B;
+      enter_table(t);
+    }
+    float acc[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    // this bag's first id batch was prefetched; start fetching the next
+    // bag's (also when this bag is empty)
+    const int64_t fid = nid;
+    const float fw = nw;
+    if (i + 1 < nb) {
+      const int64_t q0 = lane_i64(lp0, i + 1), q1 = lane_i64(lp1, i + 1);
+      nid = 0;
+      nw = 0.0f;
+      if (lane < q1 - q0) {
+        nid = load_index<IdxT>(indices, q0 + lane);
+        nw = weights ? weights[q0 + lane] : 1.0f;
+      }
+    }
+    for (int64_t c0 = p0; c0 < p1; c0 += kWave) {
+      const int n = (int)((p1 - c0) < kWave ? (p1 - c0) : kWave);
+      int64_t id = fid;
+      float wl = fw;
+      if (c0 != p0 && lane < n) {
+        id = load_index<IdxT>(indices, c0 + lane);
+        wl = weights ? weights[c0 + lane] : 1.0f;
+      }
+      int64_t off = -1;
+      if (lane < n) {
+        if (id >= 0 && id < n_t) {
+          off = id * S;
+        } else {
+          errs += 1;
+          wl = 0.0f;
+        }
+      }
+      moff[lane] = off;
+      mw[lane] = wl;
+      wave_sync_lds();
+      if (n_t > 0) wave_bag_batch<BITS, LPR>(acc, tbase, C, (int)S, code_off, g, n, moff, mw);
+      wave_sync_lds();  // the next batch overwrites the metadata
+    }
+    if (i + 1 < nb) {
+      p0 = lane_i64(lp0, i + 1);
+      p1 = lane_i64(lp1, i + 1);
+    }
+
+    const int64_t b = bag - t * B;
+    float* o = out + (b * T + t) * (int64_t)dim;
+    if (RG > 1) {
+      float* rw = red[RG > 1 ? wv : 0];
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(rw + g * (LPR * EPL) + s * EPL + e) =
+            make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+      wave_sync_lds();
+      for (int e = lane; e < dim; e += kWave) {
+        float v = rw[e];
+#pragma unroll
+        for (int gg = 1; gg < RG; ++gg) v += rw[gg * (LPR * EPL) + e];
+        o[e] = v;
+      }
+      wave_sync_lds();
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e)
+        if (s * EPL + e < dim) o[s * EPL + e] = acc[e];
+    }
+  }
+  if (errs && err_count) atomicAdd(err_count, errs);
+}
+
+// Multi-hot bags of narrow rows (LPR <= 8, so a 64-id batch is at most LPR
+// rows per lane): the run-of-bags walk of bag_wave_kernel, software
+// pipelined one bag deep.  While bag i is decoded and reduced, the rows of
+// bag i+1 are loading into a second register buffer and the ids of bag i+2
+// are being fetched; row metadata is double-buffered in LDS.
+//
+// The vector-memory counter completes in issue order, so a use of bag i's
+// rows can wait for exactly those loads only if the number of loads issued
+// after them is known at compile time.  Every step therefore issues a fixed
+// set of loads in straight-line code: all LPR row slots and 64 ids from
+// clamped positions (a lane past the batch gets id 0 / weight 0 by select).
+// No loaded value is used inside a branch.
+//
+// Rows are read through a buffer descriptor of the bag's table with 32-bit
+// byte offsets; a slot without a valid row gets an offset past the
+// descriptor's range, so the hardware returns zero codes and zero scale and
+// bias for it and it adds exactly 0 (no select, no address arithmetic beyond
+// one add).  Tables of 2 GB or more use 64-bit addresses instead: such a slot
+// reads the table's first row and its scale/bias are zeroed by select.  Bags
+// longer than 64 ids finish their extra batches synchronously.  PA4: the fp16
+// parameters start on a 4-byte boundary (one dword), else two dwords are
+// merged at use.
+// v_permlane32_swap_b32 / v_permlane16_swap_b32: exchange lanes 32..63 of a
+// with lanes 0..31 of b (resp. the odd 16-lane rows of a with the even rows
+// of b).  Written as two-operand asm with both registers read-write: this
+// compiler's two-result builtins for these instructions drop the second
+// result (it reuses the first), so the builtins are not used.
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+  asm volatile("v_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+  asm volatile("v_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Sum 16 partial elements over the 8 row groups of a wave whose lanes are
+// (group g = lane bits 3..5, chunk s = bits 0..2), halving the elements kept
+// at each step: bit 5 by permlane32_swap, bit 4 by permlane16_swap, bit 3 by
+// a DPP row rotation by 8.  Afterwards lane L holds the sums of elements
+// s*16 + b5*8 + b4*4 + b3*2 + {0, 1} (b = lane bits) in r0, r1.
+__device__ __forceinline__ void reduce_scatter_g8(float (&acc)[16], int lane, float& r0, float& r1) {
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float a = acc[k], b = acc[k + 8];
+    permlane32_swap(a, b);
+    v[k] = a + b;
+  }
+  float w4[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float a = v[k], b = v[k + 4];
+    permlane16_swap(a, b);
+    w4[k] = a + b;
+  }
+  const bool h3 = (lane >> 3) & 1;
+  const float k0 = h3 ? w4[2] : w4[0], k1 = h3 ? w4[3] : w4[1];  // kept
+  const float s0 = h3 ? w4[0] : w4[2], s1 = h3 ? w4[1] : w4[3];  // sent to lane ^ 8
+  r0 = k0 + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                          0, __builtin_bit_cast(int, s0), 0x128, 0xf, 0xf, false));
+  r1 = k1 + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                          0, __builtin_bit_cast(int, s1), 0x128, 0xf, 0xf, false));
+}
+
+template <int BITS, int LPR, bool PA4>
+struct PipeRows {
+  static constexpr int SL = LPR;  // slots per lane for a full 64-row batch
+  CodeChunk<BITS, WaveBag<BITS, LPR>::VEC> cc[SL];
+  uint32_t plo[SL];
+  uint32_t phi[PA4 ? 1 : SL];
+};
+
+constexpr uint32_t kBufLimit = 0x7fffff00u;  // tables below this many bytes use descriptors
+constexpr uint32_t kBufOut = 0x80000000u;    // offset of a slot without a row (out of range)
+constexpr int kBufWord3 = 0x00020000;        // gfx9 raw-buffer descriptor word 3
+
+template <int BITS, int LPR, typename IdxT, bool PA4, bool WEIGHTED>
+__global__ __launch_bounds__(kBlock) void bag_pipe_kernel(
+    const uint8_t* __restrict__ packed, int64_t S, int64_t total_rows,
+    const int64_t* __restrict__ table_offsets, int T, int64_t B, int dim, int C,
+    const void* __restrict__ indices, const void* __restrict__ offsets, int64_t nnz,
+    const float* __restrict__ weights, float* __restrict__ out, int32_t* __restrict__ err_count,
+    int64_t n_bags) {
+  using W = WaveBag<BITS, LPR>;
+  using Rows = PipeRows<BITS, LPR, PA4>;
+  constexpr int EPL = W::EPL, RG = W::RG, SL = LPR, VEC = W::VEC;
+  static_assert(LPR <= 8, "pipelined lookup holds at most 8 rows per lane");
+  __shared__ int64_t meta_off[kWPB][2][kWave];
+  __shared__ uint32_t meta_boff[kWPB][2][kWave];
+  __shared__ float meta_w[kWPB][2][kWave];
+  __shared__ float red[LPR == 8 ? 1 : kWPB][LPR == 8 ? 1 : kWave * EPL];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / LPR, s = lane % LPR;
+  // XCD-aware block order (a bijection on [0, gridDim.x)): consecutive block
+  // ids go round-robin over the 8 XCDs, so each XCD gets a contiguous run of
+  // bags -- a few tables at a time -- and its L2 holds fewer tables' hot rows
+  const int64_t nbk = gridDim.x, xcd = blockIdx.x % 8, kk = blockIdx.x / 8;
+  const int64_t qf = nbk / 8, rr = nbk % 8;
+  const int64_t blk = xcd * qf + (xcd < rr ? xcd : rr) + kk;
+  const int64_t bag0 = (blk * kWPB + wv) * kWave;
+  if (bag0 >= n_bags) return;  // whole waves leave together
+  const int nb = (int)((n_bags - bag0) < kWave ? (n_bags - bag0) : kWave);
+  const int c4 = C & ~3;
+  const int c4n = c4 + 4 < (int)S ? c4 + 4 : (int)S - 4;
+  const uint32_t csh = (uint32_t)(C & 3);
+  const IdxT* ids = reinterpret_cast<const IdxT*>(indices);
+  int errs = 0;
+
+  int64_t lp0 = 0, lp1 = 0;
+  if (lane < nb) {
+    lp0 = load_index<IdxT>(offsets, bag0 + lane);
+    lp1 = load_index<IdxT>(offsets, bag0 + lane + 1);
+    if (!(lp0 >= 0 && lp1 >= lp0 && lp1 <= nnz)) {
+      errs += 1;
+      lp0 = lp1 = 0;
+    }
+  }
+
+  if (nnz == 0 || total_rows == 0) {
+    // no id, or no row to read: every term is skipped, every bag is +0
+    errs += (int)(lp1 - lp0);
+    for (int i = 0; i < nb; ++i) {
+      const int64_t bag = bag0 + i, t = bag / B, b = bag - t * B;
+      float* o = out + (b * T + t) * (int64_t)dim;
+      for (int e = lane; e < dim; e += kWave) o[e] = 0.0f;
+    }
+    if (errs && err_count) atomicAdd(err_count, errs);
+    return;
+  }
+  const int code_off = s * VEC < C ? s * VEC : 0;
+
+  // table of a bag: rows, a base pointer that is always a readable row, and
+  // (for tables under kBufLimit bytes) a buffer descriptor over the table
+  struct Tab {
+    int64_t t, n_t;
+    const uint8_t* base;
+    __amdgpu_buffer_rsrc_t rsrc;
+    bool buf;
+  };
+  auto table_of = [&](int64_t bag) {
+    Tab tb;
+    tb.t = bag / B;
+    const int64_t a0 = table_offsets[tb.t], a1 = table_offsets[tb.t + 1];
+    const bool ok = a0 >= 0 && a1 > a0 && a1 <= total_rows;
+    tb.n_t = ok ? a1 - a0 : 0;
+    tb.base = packed + (ok ? a0 : 0) * S;
+    const int64_t bytes = tb.n_t * S;
+    tb.buf = bytes < (int64_t)kBufLimit;
+    tb.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)tb.base, (short)0,
+                                                tb.buf ? (int)bytes : 0, kBufWord3);
+    return tb;
+  };
+  // 64 ids and weights from position q (lanes past n get id 0, weight 0)
+  auto fetch_ids = [&](int64_t q, int n, IdxT& id, float& wl) {
+    const int64_t pos = (q + lane) < nnz ? (q + lane) : nnz - 1;
+    const IdxT v = ids[pos];
+    const float wv_ = WEIGHTED ? weights[pos] : 1.0f;
+    id = lane < n ? v : (IdxT)0;
+    wl = lane < n ? wv_ : 0.0f;
+  };
+  // validate a batch and write its metadata to LDS buffer `buf`
+  auto put_meta = [&](int buf, int n, IdxT idr, float wl, int64_t n_t) {
+    const int64_t id = (int64_t)idr;
+    const bool in = lane < n;
+    const bool ok = in && id >= 0 && id < n_t;
+    errs += (in && !ok) ? 1 : 0;
+    const int64_t off = id * S;
+    meta_off[wv][buf][lane] = ok ? off : -1;
+    meta_boff[wv][buf][lane] = ok ? (uint32_t)off : kBufOut;
+    meta_w[wv][buf][lane] = ok ? wl : 0.0f;
+  };
+  // issue all SL row slots of a batch (metadata in `buf`)
+  auto issue = [&](Rows& R, int buf, const Tab& tb) {
+    if (tb.buf) {
+#pragma unroll
+      for (int u = 0; u < SL; ++u) {
+        const uint32_t bo = meta_boff[wv][buf][u * RG + g];
+        if constexpr (VEC == 8) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(tb.rsrc, bo + code_off, 0, 0);
+          R.cc[u].v = make_uint2(v[0], v[1]);
+        } else {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(tb.rsrc, bo + code_off, 0, 0);
+          R.cc[u].v = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+        R.plo[u] = __builtin_amdgcn_raw_buffer_load_b32(tb.rsrc, bo, c4, 0);
+        if (!PA4) R.phi[PA4 ? 0 : u] = __builtin_amdgcn_raw_buffer_load_b32(tb.rsrc, bo, c4n, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < SL; ++u) {
+        const int64_t off = meta_off[wv][buf][u * RG + g];
+        const uint8_t* row = tb.base + (off >= 0 ? off : 0);
+        R.cc[u].load(row + (off >= 0 ? code_off : 0));
+        R.plo[u] = *reinterpret_cast<const uint32_t*>(row + c4);
+        if (!PA4) R.phi[PA4 ? 0 : u] = *reinterpret_cast<const uint32_t*>(row + c4n);
+      }
+    }
+  };
+  // decode and accumulate a batch of n rows; with INIT the first slot sets acc
+  auto consume = [&](Rows& R, int buf, int n, const Tab& tb, float* acc, bool init) {
+    const int U = (n + RG - 1) / RG;
+    if (init) {
+      if (U == 0) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+        return;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SL; ++u) {
+      if (u < U) {
+        const int slot = u * RG + g;
+        const float wl = meta_w[wv][buf][slot];  // 0 without a valid row
+        uint32_t prm =
+            PA4 ? R.plo[u] : __builtin_amdgcn_alignbyte(R.phi[PA4 ? 0 : u], R.plo[u], csh);
+        if (!tb.buf) prm = meta_off[wv][buf][slot] >= 0 ? prm : 0u;
+        if (u == 0 && init) {
+          accumulate<BITS, VEC, true>(acc, R.cc[u], wl, prm);
+        } else {
+          accumulate<BITS, VEC>(acc, R.cc[u], wl, prm);
+        }
+      }
+    }
+  };
+  auto batch_len = [&](int64_t from, int64_t to) {
+    return (int)((to - from) < kWave ? (to - from) : kWave);
+  };
+
+  Rows RA, RB;
+  // prologue: bag 0's first batch in flight, ids of bag 1 requested
+  Tab tc = table_of(bag0);
+  int64_t cp0 = lane_i64(lp0, 0), cp1 = lane_i64(lp1, 0);
+  int cn = batch_len(cp0, cp1);
+  {
+    IdxT id;
+    float wl;
+    fetch_ids(cp0, cn, id, wl);
+    put_meta(0, cn, id, wl, tc.n_t);
+    wave_sync_lds();
+    issue(RA, 0, tc);
+  }
+  IdxT nid;
+  float nw;
+  {
+    const bool has = nb > 1;
+    const int64_t q0 = has ? lane_i64(lp0, 1) : 0, q1 = has ? lane_i64(lp1, 1) : 0;
+    fetch_ids(q0, batch_len(q0, q1), nid, nw);
+  }
+
+  // one pipeline step: bag i (rows in Rc, metadata in buffer i&1) is
+  // finished while bag i+1's rows go out into Rn
+  auto step = [&](int i, Rows& Rc, Rows& Rn) {
+    const int cb = i & 1;
+    const bool has1 = i + 1 < nb, has2 = i + 2 < nb;
+    Tab tn = tc;
+    if (has1 && (bag0 + i + 1) / B != tc.t) tn = table_of(bag0 + i + 1);
+    const int64_t np0 = has1 ? lane_i64(lp0, i + 1) : 0;
+    const int64_t np1 = has1 ? lane_i64(lp1, i + 1) : 0;
+    const int nn = batch_len(np0, np1);
+    put_meta(cb ^ 1, nn, nid, nw, tn.n_t);
+    wave_sync_lds();
+    issue(Rn, cb ^ 1, tn);
+    {
+      const int64_t q0 = has2 ? lane_i64(lp0, i + 2) : 0;
+      const int64_t q1 = has2 ? lane_i64(lp1, i + 2) : 0;
+      fetch_ids(q0, batch_len(q0, q1), nid, nw);
+    }
+    float acc[EPL];
+    consume(Rc, cb, cn, tc, acc, true);
+    // ids past the first 64 of this bag (rare): synchronous batches
+    for (int64_t c0 = cp0 + kWave; c0 < cp1; c0 += kWave) {
+      const int n = batch_len(c0, cp1);
+      IdxT id;
+      float wl;
+      fetch_ids(c0, n, id, wl);
+      wave_sync_lds();
+      put_meta(cb, n, id, wl, tc.n_t);
+      wave_sync_lds();
+      issue(Rc, cb, tc);
+      consume(Rc, cb, n, tc, acc, false);
+    }
+    const int64_t bag = bag0 + i;
+    const int64_t b = bag - tc.t * B;
+    float* o = out + (b * T + tc.t) * (int64_t)dim;
+    if constexpr (LPR == 8) {
+      // 8 row groups: in-register reduce-scatter, one 8-byte store per lane
+      float r0, r1;
+      reduce_scatter_g8(acc, lane, r0, r1);
+      const int e0 = s * 16 + ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2;
+      if (e0 + 1 < dim) {
+        if ((dim & 1) == 0) {
+          *reinterpret_cast<float2*>(o + e0) = make_float2(r0, r1);
+        } else {
+          o[e0] = r0;
+          o[e0 + 1] = r1;
+        }
+      } else if (e0 < dim) {
+        o[e0] = r0;
+      }
+    } else {
+      float* rw = red[wv];
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4)
+        *reinterpret_cast<float4*>(rw + g * (LPR * EPL) + s * EPL + e) =
+            make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+      wave_sync_lds();
+      for (int e = lane; e < dim; e += kWave) {
+        float v = rw[e];
+#pragma unroll
+        for (int gg = 1; gg < RG; ++gg) v += rw[gg * (LPR * EPL) + e];
+        o[e] = v;
+      }
+      wave_sync_lds();
+    }
+    tc = tn;
+    cp0 = np0;
+    cp1 = np1;
+    cn = nn;
+  };
+
+  for (int i = 0; i < nb; i += 2) {
+    step(i, RA, RB);
+    if (i + 1 < nb) step(i + 1, RB, RA);
   }
   if (errs && err_count) atomicAdd(err_count, errs);
 }
@@ -549,7 +1132,7 @@ __global__ __launch_bounds__(kBlock) void l2_partial_kernel(const float* __restr
        row += (int64_t)gridDim.x * kBlock) {
     const float* xr = x + row * dim;
     const uint8_t* prow = packed + row * (int64_t)S;
-    const uint32_t p = load_params(prow, C);
+    const uint32_t p = load_params(prow, C, S);
     const float sf = half_value(p), bf = half_value(p >> 16);
     double e2 = 0.0, x2 = 0.0;
     for (int k = 0; k < dim; ++k) {
@@ -725,42 +1308,104 @@ struct BagArgs {
 
 constexpr int kBagUnroll = 4;
 
-template <int BITS, int VEC, int LPR, int RG>
-int launch_bag(const BagArgs& a, hipStream_t st) {
+template <int BITS, int VEC, int LPR, int RG, typename IdxT>
+int launch_bag_slice_t(const BagArgs& a, hipStream_t st) {
   constexpr int SLICE = LPR * RG;
   const int64_t threads = a.n_bags * SLICE;
   const int64_t blocks = (threads + kBlock - 1) / kBlock;
   if (blocks > 0x7fffffff) return QEMB_E_UNSUPPORTED;
-  hipLaunchKernelGGL((bag_kernel<BITS, VEC, LPR, RG, kBagUnroll>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((bag_slice_kernel<BITS, VEC, LPR, RG, kBagUnroll, IdxT>), dim3((unsigned)blocks),
                      dim3(kBlock), 0, st, a.packed, a.S, a.total_rows, a.table_offsets, a.T, a.B,
-                     a.dim, a.C, a.indices, a.offsets, a.idx64, a.nnz, a.weights, a.out,
+                     a.dim, a.C, a.indices, a.offsets, a.nnz, a.weights, a.out,
                      a.err_count, a.n_bags, a.vec4);
   return launched();
 }
 
+template <int BITS, int VEC, int LPR, int RG>
+int launch_bag_slice(const BagArgs& a, hipStream_t st) {
+  if (a.idx64) return launch_bag_slice_t<BITS, VEC, LPR, RG, int64_t>(a, st);
+  return launch_bag_slice_t<BITS, VEC, LPR, RG, int32_t>(a, st);
+}
+
 template <int BITS, int VEC, int LPR>
-int dispatch_bag_rg(const BagArgs& a, int rg, hipStream_t st) {
+int dispatch_slice_rg(const BagArgs& a, int rg, hipStream_t st) {
   constexpr int MAXRG = (64 / LPR) < 16 ? (64 / LPR) : 16;
   if (rg > MAXRG) rg = MAXRG;
   switch (rg) {
-    case 1: return launch_bag<BITS, VEC, LPR, 1>(a, st);
-    case 2: return launch_bag<BITS, VEC, LPR, (2 <= MAXRG ? 2 : 1)>(a, st);
-    case 4: return launch_bag<BITS, VEC, LPR, (4 <= MAXRG ? 4 : 1)>(a, st);
-    case 8: return launch_bag<BITS, VEC, LPR, (8 <= MAXRG ? 8 : 1)>(a, st);
-    default: return launch_bag<BITS, VEC, LPR, (16 <= MAXRG ? 16 : 1)>(a, st);
+    case 1: return launch_bag_slice<BITS, VEC, LPR, 1>(a, st);
+    case 2: return launch_bag_slice<BITS, VEC, LPR, (2 <= MAXRG ? 2 : 1)>(a, st);
+    case 4: return launch_bag_slice<BITS, VEC, LPR, (4 <= MAXRG ? 4 : 1)>(a, st);
+    case 8: return launch_bag_slice<BITS, VEC, LPR, (8 <= MAXRG ? 8 : 1)>(a, st);
+    default: return launch_bag_slice<BITS, VEC, LPR, (16 <= MAXRG ? 16 : 1)>(a, st);
   }
 }
 
 template <int BITS, int VEC>
-int dispatch_bag_lpr(const BagArgs& a, int lpr, int rg, hipStream_t st) {
+int dispatch_slice(const BagArgs& a, int lpr, int rg, hipStream_t st) {
   switch (lpr) {
-    case 1: return dispatch_bag_rg<BITS, VEC, 1>(a, rg, st);
-    case 2: return dispatch_bag_rg<BITS, VEC, 2>(a, rg, st);
-    case 4: return dispatch_bag_rg<BITS, VEC, 4>(a, rg, st);
-    case 8: return dispatch_bag_rg<BITS, VEC, 8>(a, rg, st);
-    case 16: return dispatch_bag_rg<BITS, VEC, 16>(a, rg, st);
-    case 32: return dispatch_bag_rg<BITS, VEC, 32>(a, rg, st);
-    default: return dispatch_bag_rg<BITS, VEC, 64>(a, rg, st);
+    case 1: return dispatch_slice_rg<BITS, VEC, 1>(a, rg, st);
+    case 2: return dispatch_slice_rg<BITS, VEC, 2>(a, rg, st);
+    case 4: return dispatch_slice_rg<BITS, VEC, 4>(a, rg, st);
+    case 8: return dispatch_slice_rg<BITS, VEC, 8>(a, rg, st);
+    case 16: return dispatch_slice_rg<BITS, VEC, 16>(a, rg, st);
+    case 32: return dispatch_slice_rg<BITS, VEC, 32>(a, rg, st);
+    default: return dispatch_slice_rg<BITS, VEC, 64>(a, rg, st);
+  }
+}
+
+template <int BITS, int LPR, typename IdxT>
+int launch_bag_wave_t(const BagArgs& a, hipStream_t st) {
+  const int64_t blocks = (a.n_bags + kWPB * kWave - 1) / (kWPB * kWave);
+  if (blocks > 0x7fffffff) return QEMB_E_UNSUPPORTED;
+  hipLaunchKernelGGL((bag_wave_kernel<BITS, LPR, IdxT>), dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                     a.packed, a.S, a.total_rows, a.table_offsets, a.T, a.B, a.dim, a.C, a.indices,
+                     a.offsets, a.nnz, a.weights, a.out, a.err_count, a.n_bags);
+  return launched();
+}
+
+template <int BITS, int LPR, typename IdxT, bool PA4, bool WEIGHTED>
+int launch_bag_pipe_w(const BagArgs& a, hipStream_t st) {
+  const int64_t blocks = (a.n_bags + kWPB * kWave - 1) / (kWPB * kWave);
+  if (blocks > 0x7fffffff) return QEMB_E_UNSUPPORTED;
+  hipLaunchKernelGGL((bag_pipe_kernel<BITS, LPR, IdxT, PA4, WEIGHTED>), dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                     a.packed, a.S, a.total_rows, a.table_offsets, a.T, a.B, a.dim, a.C, a.indices,
+                     a.offsets, a.nnz, a.weights, a.out, a.err_count, a.n_bags);
+  return launched();
+}
+
+template <int BITS, int LPR, typename IdxT, bool PA4>
+int launch_bag_pipe_t(const BagArgs& a, hipStream_t st) {
+  return a.weights ? launch_bag_pipe_w<BITS, LPR, IdxT, PA4, true>(a, st)
+                   : launch_bag_pipe_w<BITS, LPR, IdxT, PA4, false>(a, st);
+}
+
+template <int BITS, int LPR>
+int launch_bag_wave(const BagArgs& a, hipStream_t st) {
+  return a.idx64 ? launch_bag_wave_t<BITS, LPR, int64_t>(a, st)
+                 : launch_bag_wave_t<BITS, LPR, int32_t>(a, st);
+}
+
+template <int BITS, int LPR>
+int launch_bag_pipe(const BagArgs& a, hipStream_t st) {
+  if (a.C % 4 == 0)
+    return a.idx64 ? launch_bag_pipe_t<BITS, LPR, int64_t, true>(a, st)
+                   : launch_bag_pipe_t<BITS, LPR, int32_t, true>(a, st);
+  return a.idx64 ? launch_bag_pipe_t<BITS, LPR, int64_t, false>(a, st)
+                 : launch_bag_pipe_t<BITS, LPR, int32_t, false>(a, st);
+}
+
+template <int BITS>
+int dispatch_wave(const BagArgs& a, hipStream_t st) {
+  constexpr int VEC = WaveBag<BITS, 1>::VEC;
+  const int lpr = next_pow2((a.C + VEC - 1) / VEC);
+  switch (lpr) {
+    case 1: return launch_bag_pipe<BITS, 1>(a, st);
+    case 2: return launch_bag_pipe<BITS, 2>(a, st);
+    case 4: return launch_bag_pipe<BITS, 4>(a, st);
+    case 8: return launch_bag_pipe<BITS, 8>(a, st);
+    case 16: return launch_bag_wave<BITS, 16>(a, st);
+    case 32: return launch_bag_wave<BITS, 32>(a, st);
+    default: return launch_bag_wave<BITS, 64>(a, st);
   }
 }
 
@@ -864,16 +1509,18 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
   a.n_bags = (int64_t)T * B;
   a.vec4 = (dim % 4 == 0);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // lanes per row: 8-byte code chunks (16-byte for INT8 rows wider than 512)
+  // multi-hot bags (8+ ids on average): one wave per bag
+  const int64_t mean_len = (nnz + a.n_bags - 1) / a.n_bags;
+  if (mean_len >= 8) return bits == 4 ? dispatch_wave<4>(a, st) : dispatch_wave<8>(a, st);
+  // short bags: several bags per wave; 8-byte code chunks per lane (16-byte
+  // for INT8 rows wider than 512 codes), about kBagUnroll rows per group
   const int64_t chunks8 = (a.C + 7) / 8;
   const int vec = chunks8 > 64 ? 16 : 8;
   const int lpr = next_pow2((a.C + vec - 1) / vec);
-  // row groups per bag: about kBagUnroll rows per group for the mean bag
-  const int64_t mean_len = (nnz + a.n_bags - 1) / a.n_bags;
   const int rg = next_pow2((mean_len + kBagUnroll - 1) / kBagUnroll);
-  if (bits == 4) return dispatch_bag_lpr<4, 8>(a, lpr, rg, st);
-  if (vec == 8) return dispatch_bag_lpr<8, 8>(a, lpr, rg, st);
-  return dispatch_bag_rg<8, 16, 64>(a, rg, st);  // only rows wider than 512 codes get here
+  if (bits == 4) return dispatch_slice<4, 8>(a, lpr, rg, st);
+  if (vec == 8) return dispatch_slice<8, 8>(a, lpr, rg, st);
+  return dispatch_slice_rg<8, 16, 64>(a, rg, st);  // only rows wider than 512 codes get here
 }
 
 size_t qemb_l2_error_workspace_bytes(void) { return (size_t)kL2Blocks * 4 * sizeof(double); }
