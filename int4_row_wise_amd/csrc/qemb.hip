@@ -5,8 +5,9 @@
 //   * quantize_greedy_kernel  greedy clip search on the row's squared error,
 //                             then the same encoding
 //   * dequant_kernel          packed rows -> fp32
-//   * bag_wave_kernel         fused decode + (weighted) sum pooling, one wave per
-//                             multi-hot bag
+//   * bag_stream_kernel       fused decode + (weighted) sum pooling of multi-hot
+//                             bags, pipelined over batches of ids
+//   * bag_wave_kernel         the same for rows wider than 8 lanes
 //   * bag_slice_kernel        the same for short bags, several bags per wave
 //   * l2_partial/l2_final     normalized l2 error, fixed-order reduction
 //
@@ -25,6 +26,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "qemb.h"
 
@@ -775,38 +778,19 @@ __global__ __launch_bounds__(kBlock) void bag_wave_kernel(
   if (errs && err_count) atomicAdd(err_count, errs);
 }
 
-// Multi-hot bags of narrow rows (LPR <= 8, so a 64-id batch is at most LPR
-// rows per lane): the run-of-bags walk of bag_wave_kernel, software
-// pipelined one bag deep.  While bag i is decoded and reduced, the rows of
-// bag i+1 are loading into a second register buffer and the ids of bag i+2
-// are being fetched; row metadata is double-buffered in LDS.
-//
-// The vector-memory counter completes in issue order, so a use of bag i's
-// rows can wait for exactly those loads only if the number of loads issued
-// after them is known at compile time.  Every step therefore issues a fixed
-// set of loads in straight-line code: all LPR row slots and 64 ids from
-// clamped positions (a lane past the batch gets id 0 / weight 0 by select).
-// No loaded value is used inside a branch.
-//
-// Rows are read through a buffer descriptor of the bag's table with 32-bit
-// byte offsets; a slot without a valid row gets an offset past the
-// descriptor's range, so the hardware returns zero codes and zero scale and
-// bias for it and it adds exactly 0 (no select, no address arithmetic beyond
-// one add).  Tables of 2 GB or more use 64-bit addresses instead: such a slot
-// reads the table's first row and its scale/bias are zeroed by select.  Bags
-// longer than 64 ids finish their extra batches synchronously.  PA4: the fp16
-// parameters start on a 4-byte boundary (one dword), else two dwords are
-// merged at use.
 // v_permlane32_swap_b32 / v_permlane16_swap_b32: exchange lanes 32..63 of a
 // with lanes 0..31 of b (resp. the odd 16-lane rows of a with the even rows
 // of b).  Written as two-operand asm with both registers read-write: this
 // compiler's two-result builtins for these instructions drop the second
-// result (it reuses the first), so the builtins are not used.
+// result (it reuses the first), so the builtins are not used.  The compiler
+// inserts no wait states before inline asm, and on gfx950 these swaps read
+// their operands wrongly within 2 wait states of a VALU write to them (4 of
+// a v_cmpx write to exec), so each swap starts with s_nop 3 (4 wait states).
 __device__ __forceinline__ void permlane32_swap(float& a, float& b) {
-  asm volatile("v_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 3\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 __device__ __forceinline__ void permlane16_swap(float& a, float& b) {
-  asm volatile("v_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  asm volatile("s_nop 3\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
 // Sum 16 partial elements over the 8 row groups of a wave whose lanes are
@@ -815,55 +799,202 @@ __device__ __forceinline__ void permlane16_swap(float& a, float& b) {
 // a DPP row rotation by 8.  Afterwards lane L holds the sums of elements
 // s*16 + b5*8 + b4*4 + b3*2 + {0, 1} (b = lane bits) in r0, r1.
 __device__ __forceinline__ void reduce_scatter_g8(float (&acc)[16], int lane, float& r0, float& r1) {
-  float v[8];
+  // in place: acc is consumed
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    float a = acc[k], b = acc[k + 8];
-    permlane32_swap(a, b);
-    v[k] = a + b;
+    permlane32_swap(acc[k], acc[k + 8]);
+    acc[k] += acc[k + 8];
   }
-  float w4[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    float a = v[k], b = v[k + 4];
-    permlane16_swap(a, b);
-    w4[k] = a + b;
+    permlane16_swap(acc[k], acc[k + 4]);
+    acc[k] += acc[k + 4];
   }
   const bool h3 = (lane >> 3) & 1;
-  const float k0 = h3 ? w4[2] : w4[0], k1 = h3 ? w4[3] : w4[1];  // kept
-  const float s0 = h3 ? w4[0] : w4[2], s1 = h3 ? w4[1] : w4[3];  // sent to lane ^ 8
+  const float k0 = h3 ? acc[2] : acc[0], k1 = h3 ? acc[3] : acc[1];  // kept
+  const float s0 = h3 ? acc[0] : acc[2], s1 = h3 ? acc[1] : acc[3];  // sent to lane ^ 8
   r0 = k0 + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                                           0, __builtin_bit_cast(int, s0), 0x128, 0xf, 0xf, false));
   r1 = k1 + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                                           0, __builtin_bit_cast(int, s1), 0x128, 0xf, 0xf, false));
 }
 
-template <int BITS, int LPR, bool PA4>
-struct PipeRows {
-  static constexpr int SL = LPR;  // slots per lane for a full 64-row batch
-  CodeChunk<BITS, WaveBag<BITS, LPR>::VEC> cc[SL];
-  uint32_t plo[SL];
-  uint32_t phi[PA4 ? 1 : SL];
+// Multi-hot bags of narrow rows (LPR <= 8): each wave streams the ids of a
+// run of 64 consecutive bags as a sequence of batches of up to BATCH ids
+// (BATCH = RG row groups x SLOTS rows per lane, at most 64).  A bag is one or
+// more batches (an empty bag is one empty batch), so long bags need no
+// special path.  The batch stream is software pipelined DEPTH batches deep:
+// while batch k is decoded, the rows of batches k+1 .. k+DEPTH are loading
+// into rotating register buffers and the ids of batch k+DEPTH+1 are being
+// fetched.  A bag's accumulators carry across its batches; at its last batch
+// the RG partial vectors are summed and stored.  All batch bookkeeping
+// (positions, bag and table cursors, flags) is wave-uniform and lives in
+// scalar registers.
+//
+// Lane L of a batch owns id L: it validates it, computes the row's byte
+// offset, and loads the row's scale/bias dword; the lanes that read row L's
+// codes (and later decode them) get the offset, the weight and the scale/bias
+// from lane L by ds_bpermute.
+//
+// The vector-memory counter completes in issue order, so a use can wait for
+// exactly the loads it needs only if the number of loads issued after them
+// is fixed.  Every step therefore issues the same loads in straight-line
+// code: the next batch's ids (and weights) through a buffer descriptor that
+// spans exactly that batch (lanes past it read 0), then the scale/bias dword
+// and all SLOTS row slots.  The ids go out before the rows, so waiting for
+// them (next step) does not wait for the rows still in flight.  No loaded
+// value is used inside a branch.
+//
+// Rows are read through a buffer descriptor of the batch's table with 32-bit
+// byte offsets; a slot without a valid row gets an offset past the
+// descriptor's range, so the hardware returns zero codes and zero scale and
+// bias.  Tables of 2 GB or more use 64-bit addresses instead (such a slot
+// reads the table's first row).  Either way a lane whose id is not a valid
+// row has weight 0 and its scale/bias is replaced by 0 before it is handed
+// out, so the row adds exactly 0.  PA4: the scale/bias starts on a 4-byte
+// boundary (one dword), else two dwords are merged.
+// A wave-uniform condition from a 64-bit signed comparison (evaluated by the
+// VALU into VCC), turned into a 0/1 integer in an SGPR that the compiler
+// cannot see through.  Used where such a condition feeds scalar selects: this
+// compiler has emitted s_cselect on a stale SCC for them (after dropping the
+// s_and of VCC with EXEC that sets SCC) in unrolled copies of the loop.
+__device__ __forceinline__ bool uniform_flag(bool c) {
+  int v = __builtin_amdgcn_readfirstlane(c ? 1 : 0);
+  asm volatile("" : "+s"(v));
+  return v != 0;
+}
+
+template <int BITS, int LPR>
+struct StreamGeo {
+  static constexpr int RG = kWave / LPR;
+  static constexpr int SLOTS = LPR;          // RG * SLOTS = 64 ids per batch
+  static constexpr int BATCH = RG * SLOTS;
+  static constexpr int VEC = WaveBag<BITS, LPR>::VEC;
+  static constexpr int EPL = WaveBag<BITS, LPR>::EPL;
+  // batches whose rows are in flight beyond the one being decoded (64-id
+  // batches: one more batch keeps about 2x32 rows per wave in flight; deeper
+  // rings cost registers, hence occupancy, and measured no faster)
+  static constexpr int DEPTH = 1;
 };
+
+// PX: each lane's slot load also takes the 4 bytes after its codes, which in
+// a row's last lane are the row's scale and bias (rows whose codes fill the
+// LPR lanes exactly and end on a 4-byte boundary).  Otherwise lane L loads
+// the scale/bias of batch row L itself, one dword from each of 64 rows.
+template <int BITS, int LPR, bool PA4, bool PX>
+struct StreamRows {
+  CodeChunk<BITS, StreamGeo<BITS, LPR>::VEC> cc[StreamGeo<BITS, LPR>::SLOTS];
+  uint32_t px[PX ? StreamGeo<BITS, LPR>::SLOTS : 1];  // PX: the dword after each lane's codes
+  uint32_t plo, phi;  // not PX: scale/bias dword(s) of batch row `lane`
+  float w;            // weight of batch row `lane` (0 without a valid row)
+};
+
+// Centered decode.  A row's decoded values are y = bf + sf*q.  With m the
+// code nearest the row's zero crossing (clamped to [0, Q]) and
+// c = fma(sf, m, bf), y = c + sf*(q - m), and |c| <= |y| for every code of the
+// row (either c is the value of code m itself, at most sf/2 from zero, or the
+// whole row lies on one side of zero and c is its value nearest zero), while
+// |sf*(q - m)| <= |y| + |c| <= 2|y|.  A bag's pooled element is accumulated
+// as sum_r fl(w_r sf_r)*(q - m_r) per element plus sum_r fl(w_r c_r) once per
+// bag, so every summed quantity is bounded by 2|w y| and the fp32 rounding
+// error stays a small multiple of eps * sum|w y| -- the bound the direct form
+// sum fl(w * fl(bf + sf*q)) has -- while the per-element work drops to one
+// v_fma_mix (fp32 ws times an fp16 integer) plus the unpack.
+//
+// Unpack: a code k placed in the low mantissa bits of fp16 0x6400 reads as
+// 1024 + k; one packed fp16 add of -(1024 + m) (-(1024 + 16 m) for a code in
+// bits 4..7, which reads as 1024 + 16k) leaves k - m (16(k - m)) exactly, two
+// elements per instruction.  The 16(k - m) halves are scaled by ws/16, which
+// is exact, so every element's product is ws*(k - m) exactly before the one
+// rounding of its fma.
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
+
+// The masks and the 0x64006400 pattern are passed in registers (UnpackK):
+// with both as literals the compiler splits each v_and_or_b32 in two.
+struct UnpackK {
+  uint32_t m_lo, m_hi, m_byte, one;
+};
+
+template <int BITS, int VEC, bool INIT = false>
+__device__ __forceinline__ void accumulate_centered(float* acc, const CodeChunk<BITS, VEC>& c, float ws,
+                                                    uint32_t nlo, uint32_t nhi, const UnpackK& K) {
+  const half2v hlo = as_h2(nlo);
+#pragma unroll
+  for (int d = 0; d < VEC / 4; ++d) {
+    const uint32_t x = c.dw(d), x8 = x >> 8;
+    if constexpr (BITS == 4) {
+      const half2v hhi = as_h2(nhi);
+      const float ws16 = ws * 0.0625f;
+      const half2v a = as_h2((x & K.m_lo) | K.one) + hlo;   // elements 0, 4
+      const half2v b = as_h2((x & K.m_hi) | K.one) + hhi;   // 1, 5 (x16)
+      const half2v e = as_h2((x8 & K.m_lo) | K.one) + hlo;  // 2, 6
+      const half2v f = as_h2((x8 & K.m_hi) | K.one) + hhi;  // 3, 7 (x16)
+      float* o = acc + 8 * d;
+      o[0] = __builtin_fmaf(ws, (float)a.x, INIT ? 0.0f : o[0]);
+      o[1] = __builtin_fmaf(ws16, (float)b.x, INIT ? 0.0f : o[1]);
+      o[2] = __builtin_fmaf(ws, (float)e.x, INIT ? 0.0f : o[2]);
+      o[3] = __builtin_fmaf(ws16, (float)f.x, INIT ? 0.0f : o[3]);
+      o[4] = __builtin_fmaf(ws, (float)a.y, INIT ? 0.0f : o[4]);
+      o[5] = __builtin_fmaf(ws16, (float)b.y, INIT ? 0.0f : o[5]);
+      o[6] = __builtin_fmaf(ws, (float)e.y, INIT ? 0.0f : o[6]);
+      o[7] = __builtin_fmaf(ws16, (float)f.y, INIT ? 0.0f : o[7]);
+    } else {
+      const half2v a = as_h2((x & K.m_byte) | K.one) + hlo;   // elements 0, 2
+      const half2v b = as_h2((x8 & K.m_byte) | K.one) + hlo;  // 1, 3
+      float* o = acc + 4 * d;
+      o[0] = __builtin_fmaf(ws, (float)a.x, INIT ? 0.0f : o[0]);
+      o[1] = __builtin_fmaf(ws, (float)b.x, INIT ? 0.0f : o[1]);
+      o[2] = __builtin_fmaf(ws, (float)a.y, INIT ? 0.0f : o[2]);
+      o[3] = __builtin_fmaf(ws, (float)b.y, INIT ? 0.0f : o[3]);
+    }
+  }
+}
+
+// Sum of v over the 64 lanes of the wave, in every lane: DPP within each
+// 16-lane row, then the permlane swaps across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  float a = v, b = v;
+  permlane32_swap(a, b);
+  v = a + b;
+  a = v;
+  b = v;
+  permlane16_swap(a, b);
+  return a + b;
+}
 
 constexpr uint32_t kBufLimit = 0x7fffff00u;  // tables below this many bytes use descriptors
 constexpr uint32_t kBufOut = 0x80000000u;    // offset of a slot without a row (out of range)
 constexpr int kBufWord3 = 0x00020000;        // gfx9 raw-buffer descriptor word 3
 
-template <int BITS, int LPR, typename IdxT, bool PA4, bool WEIGHTED>
-__global__ __launch_bounds__(kBlock) void bag_pipe_kernel(
+__device__ __forceinline__ uint32_t bperm(int addr, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v);
+}
+
+template <int BITS, int LPR, typename IdxT, bool PA4, bool WEIGHTED, bool PX>
+__global__ __launch_bounds__(kBlock) void bag_stream_kernel(
     const uint8_t* __restrict__ packed, int64_t S, int64_t total_rows,
     const int64_t* __restrict__ table_offsets, int T, int64_t B, int dim, int C,
     const void* __restrict__ indices, const void* __restrict__ offsets, int64_t nnz,
     const float* __restrict__ weights, float* __restrict__ out, int32_t* __restrict__ err_count,
     int64_t n_bags) {
-  using W = WaveBag<BITS, LPR>;
-  using Rows = PipeRows<BITS, LPR, PA4>;
-  constexpr int EPL = W::EPL, RG = W::RG, SL = LPR, VEC = W::VEC;
-  static_assert(LPR <= 8, "pipelined lookup holds at most 8 rows per lane");
-  __shared__ int64_t meta_off[kWPB][2][kWave];
-  __shared__ uint32_t meta_boff[kWPB][2][kWave];
-  __shared__ float meta_w[kWPB][2][kWave];
+  using G = StreamGeo<BITS, LPR>;
+  using Rows = StreamRows<BITS, LPR, PA4, PX>;
+  static_assert(!PX || (StreamGeo<BITS, LPR>::VEC == 8 && PA4), "PX: 8-byte lane chunks, aligned scale/bias");
+  constexpr int EPL = G::EPL, RG = G::RG, SLOTS = G::SLOTS, BATCH = G::BATCH, VEC = G::VEC;
+  constexpr int DEPTH = G::DEPTH, NBUF = DEPTH + 1;
+  static_assert(LPR <= 8 && EPL == 16, "stream lookup: 16 elements per lane, <= 8 lanes per row");
   __shared__ float red[LPR == 8 ? 1 : kWPB][LPR == 8 ? 1 : kWave * EPL];
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
@@ -892,6 +1023,7 @@ __global__ __launch_bounds__(kBlock) void bag_pipe_kernel(
       lp0 = lp1 = 0;
     }
   }
+  const int64_t t0 = bag0 / B, b0 = bag0 - t0 * B;
 
   if (nnz == 0 || total_rows == 0) {
     // no id, or no row to read: every term is skipped, every bag is +0
@@ -905,177 +1037,219 @@ __global__ __launch_bounds__(kBlock) void bag_pipe_kernel(
     return;
   }
   const int code_off = s * VEC < C ? s * VEC : 0;
-
-  // table of a bag: rows, a base pointer that is always a readable row, and
-  // (for tables under kBufLimit bytes) a buffer descriptor over the table
-  struct Tab {
-    int64_t t, n_t;
-    const uint8_t* base;
-    __amdgpu_buffer_rsrc_t rsrc;
-    bool buf;
-  };
-  auto table_of = [&](int64_t bag) {
-    Tab tb;
-    tb.t = bag / B;
-    const int64_t a0 = table_offsets[tb.t], a1 = table_offsets[tb.t + 1];
-    const bool ok = a0 >= 0 && a1 > a0 && a1 <= total_rows;
-    tb.n_t = ok ? a1 - a0 : 0;
-    tb.base = packed + (ok ? a0 : 0) * S;
-    const int64_t bytes = tb.n_t * S;
-    tb.buf = bytes < (int64_t)kBufLimit;
-    tb.rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)tb.base, (short)0,
-                                                tb.buf ? (int)bytes : 0, kBufWord3);
-    return tb;
-  };
-  // 64 ids and weights from position q (lanes past n get id 0, weight 0)
-  auto fetch_ids = [&](int64_t q, int n, IdxT& id, float& wl) {
-    const int64_t pos = (q + lane) < nnz ? (q + lane) : nnz - 1;
-    const IdxT v = ids[pos];
-    const float wv_ = WEIGHTED ? weights[pos] : 1.0f;
-    id = lane < n ? v : (IdxT)0;
-    wl = lane < n ? wv_ : 0.0f;
-  };
-  // validate a batch and write its metadata to LDS buffer `buf`
-  auto put_meta = [&](int buf, int n, IdxT idr, float wl, int64_t n_t) {
-    const int64_t id = (int64_t)idr;
-    const bool in = lane < n;
-    const bool ok = in && id >= 0 && id < n_t;
-    errs += (in && !ok) ? 1 : 0;
-    const int64_t off = id * S;
-    meta_off[wv][buf][lane] = ok ? off : -1;
-    meta_boff[wv][buf][lane] = ok ? (uint32_t)off : kBufOut;
-    meta_w[wv][buf][lane] = ok ? wl : 0.0f;
-  };
-  // issue all SL row slots of a batch (metadata in `buf`)
-  auto issue = [&](Rows& R, int buf, const Tab& tb) {
-    if (tb.buf) {
+  int baddr[SLOTS];  // ds_bpermute address of batch row u*RG + g
 #pragma unroll
-      for (int u = 0; u < SL; ++u) {
-        const uint32_t bo = meta_boff[wv][buf][u * RG + g];
-        if constexpr (VEC == 8) {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b64(tb.rsrc, bo + code_off, 0, 0);
+  for (int u = 0; u < SLOTS; ++u) baddr[u] = (u * RG + g) * 4;
+  const int aown = ((lane % RG) * LPR + LPR - 1) * 4;  // PX: the lane holding row lane's scale/bias
+
+  // ---- producer cursor: the next batch to generate (wave-uniform) ----
+  int gj = 0;                                            // its bag within the run
+  int64_t gpos = lane_i64(lp0, 0), gend = lane_i64(lp1, 0);
+  int gfirst = 1;
+  int64_t gt = t0, gb = b0;                              // table, row of the bag
+  // a batch: its id count, its table (-1: past the run) and flags
+  constexpr int kFirst = 1, kLast = 2, kReal = 4;  // first / last batch of its bag; in the run
+  struct Batch {
+    int n, t, f;
+  };
+  auto next_batch = [&](IdxT& id, float& wl) {
+    Batch bt;
+    int64_t q = 0;
+    if (gj < nb) {
+      const int64_t rem = gend - gpos;
+      const bool last = uniform_flag(rem <= BATCH);
+      q = gpos;
+      bt.n = last ? (int)rem : BATCH;
+      bt.t = (int)gt;
+      bt.f = gfirst | (last ? kLast : 0) | kReal;
+      if (last) {
+        ++gj;
+        if (++gb == B) {
+          gb = 0;
+          ++gt;
+        }
+        gfirst = kFirst;
+        if (gj < nb) {
+          gpos = lane_i64(lp0, gj);
+          gend = lane_i64(lp1, gj);
+        }
+      } else {
+        gpos += BATCH;
+        gfirst = 0;
+      }
+    } else {
+      bt.n = 0;
+      bt.t = -1;  // keeps the current table
+      bt.f = 0;
+    }
+    // this batch's ids (and weights) through a descriptor of exactly n ids
+    const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ids + q), (short)0, bt.n * (int)sizeof(IdxT), kBufWord3);
+    if constexpr (sizeof(IdxT) == 8) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(ri, lane * 8, 0, 0);
+      id = (IdxT)(((uint64_t)v[1] << 32) | v[0]);
+    } else {
+      id = (IdxT)__builtin_amdgcn_raw_buffer_load_b32(ri, lane * 4, 0, 0);
+    }
+    if constexpr (WEIGHTED) {
+      const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(weights + q), (short)0, bt.n * 4, kBufWord3);
+      wl = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, lane * 4, 0, 0));
+    } else {
+      wl = 1.0f;
+    }
+    return bt;
+  };
+
+  // ---- the current table (the one of the batch being issued) ----
+  int tab_t = -1;
+  int64_t tab_nt = 0;
+  const uint8_t* tab_base = packed;
+  __amdgpu_buffer_rsrc_t tab_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)packed, (short)0, 0, kBufWord3);
+  auto use_table = [&](int t) {
+    if (t >= 0 && t != tab_t) {
+      tab_t = t;
+      const int64_t a0 = table_offsets[t], a1 = table_offsets[t + 1];
+      const bool ok = uniform_flag(a0 >= 0 && a1 > a0 && a1 <= total_rows);
+      tab_nt = ok ? a1 - a0 : 0;
+      tab_base = packed + (ok ? a0 : 0) * S;
+      const int64_t bytes = tab_nt * S;
+      tab_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)tab_base, (short)0, uniform_flag(bytes < (int64_t)kBufLimit) ? (int)bytes : 0, kBufWord3);
+    }
+  };
+
+  // validate lane's id of a batch; issue its scale/bias load and all slots
+  // (BUF: through the table's descriptor, else with 64-bit addresses)
+  auto issue = [&](Rows& R, const Batch& bt, IdxT idr, float wl, auto BUF_) {
+    const bool in = lane < bt.n;
+    bool ok;
+    if constexpr (sizeof(IdxT) == 8) {
+      ok = in && idr >= 0 && (int64_t)idr < tab_nt;
+    } else {
+      ok = in && (uint32_t)idr < (uint64_t)tab_nt;
+    }
+    errs += __builtin_popcountll(__ballot(in && !ok));
+    R.w = ok ? wl : 0.0f;
+    if constexpr (decltype(BUF_)::value) {
+      const uint32_t own = ok ? (uint32_t)idr * (uint32_t)S : kBufOut;
+      if constexpr (!PX) {
+        R.plo = __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, own, c4, 0);
+        if constexpr (!PA4) R.phi = __builtin_amdgcn_raw_buffer_load_b32(tab_rsrc, own, c4n, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < SLOTS; ++u) {
+        const uint32_t bo = bperm(baddr[u], own) + (uint32_t)code_off;
+        if constexpr (PX) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b96(tab_rsrc, bo, 0, 0);
+          R.cc[u].v = make_uint2(v[0], v[1]);
+          R.px[u] = v[2];
+        } else if constexpr (VEC == 8) {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(tab_rsrc, bo, 0, 0);
           R.cc[u].v = make_uint2(v[0], v[1]);
         } else {
-          const auto v = __builtin_amdgcn_raw_buffer_load_b128(tb.rsrc, bo + code_off, 0, 0);
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(tab_rsrc, bo, 0, 0);
           R.cc[u].v = make_uint4(v[0], v[1], v[2], v[3]);
         }
-        R.plo[u] = __builtin_amdgcn_raw_buffer_load_b32(tb.rsrc, bo, c4, 0);
-        if (!PA4) R.phi[PA4 ? 0 : u] = __builtin_amdgcn_raw_buffer_load_b32(tb.rsrc, bo, c4n, 0);
       }
     } else {
-#pragma unroll
-      for (int u = 0; u < SL; ++u) {
-        const int64_t off = meta_off[wv][buf][u * RG + g];
-        const uint8_t* row = tb.base + (off >= 0 ? off : 0);
-        R.cc[u].load(row + (off >= 0 ? code_off : 0));
-        R.plo[u] = *reinterpret_cast<const uint32_t*>(row + c4);
-        if (!PA4) R.phi[PA4 ? 0 : u] = *reinterpret_cast<const uint32_t*>(row + c4n);
+      const uint64_t own = ok ? (uint64_t)(int64_t)idr * (uint64_t)S : 0;
+      const uint8_t* orow = tab_base + own;
+      if constexpr (!PX) {
+        R.plo = *reinterpret_cast<const uint32_t*>(orow + c4);
+        if constexpr (!PA4) R.phi = *reinterpret_cast<const uint32_t*>(orow + c4n);
       }
-    }
-  };
-  // decode and accumulate a batch of n rows; with INIT the first slot sets acc
-  auto consume = [&](Rows& R, int buf, int n, const Tab& tb, float* acc, bool init) {
-    const int U = (n + RG - 1) / RG;
-    if (init) {
-      if (U == 0) {
+      const uint32_t olo = (uint32_t)own, ohi = (uint32_t)(own >> 32);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-        return;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < SL; ++u) {
-      if (u < U) {
-        const int slot = u * RG + g;
-        const float wl = meta_w[wv][buf][slot];  // 0 without a valid row
-        uint32_t prm =
-            PA4 ? R.plo[u] : __builtin_amdgcn_alignbyte(R.phi[PA4 ? 0 : u], R.plo[u], csh);
-        if (!tb.buf) prm = meta_off[wv][buf][slot] >= 0 ? prm : 0u;
-        if (u == 0 && init) {
-          accumulate<BITS, VEC, true>(acc, R.cc[u], wl, prm);
+      for (int u = 0; u < SLOTS; ++u) {
+        const uint64_t o = ((uint64_t)bperm(baddr[u], ohi) << 32) | bperm(baddr[u], olo);
+        if constexpr (PX) {
+          const uint3 v = *reinterpret_cast<const uint3*>(tab_base + o + code_off);
+          R.cc[u].v = make_uint2(v.x, v.y);
+          R.px[u] = v.z;
         } else {
-          accumulate<BITS, VEC>(acc, R.cc[u], wl, prm);
+          R.cc[u].load(tab_base + o + code_off);
         }
       }
     }
   };
-  auto batch_len = [&](int64_t from, int64_t to) {
-    return (int)((to - from) < kWave ? (to - from) : kWave);
+
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+  float accb = 0.0f;  // this lane's share of the bag's sum of w * c
+  bool bag_empty = false;
+  constexpr float kQ = (float)((1 << BITS) - 1);
+  UnpackK K{0x000F000Fu, 0x00F000F0u, 0x00FF00FFu, 0x64006400u};
+  asm volatile("" : "+s"(K.m_lo), "+s"(K.m_hi), "+s"(K.m_byte), "+v"(K.one));
+  // decode and accumulate a batch; its first batch starts the bag's sums (an
+  // empty bag adds nothing and is written as +0)
+  auto consume = [&](Rows& R, int nf) {
+    const int U = ((nf & 0xff) + RG - 1) / RG;
+    const bool first = nf & (kFirst << 8);
+    if (first) bag_empty = U == 0;
+    if (U == 0) return;
+    // lane L prepares batch row L: m, c, ws (zeros without a valid row:
+    // its scale/bias read as 0, or its weight is 0)
+    uint32_t pown;
+    if constexpr (PX) {
+      // row L = u*RG + g: its scale/bias came with slot u, in lane g*LPR + LPR-1
+      pown = 0u;
+#pragma unroll
+      for (int u = 0; u < SLOTS; ++u) {
+        const uint32_t t = bperm(aown, R.px[u]);
+        pown = lane / RG == u ? t : pown;
+      }
+    } else {
+      pown = PA4 ? R.plo : __builtin_amdgcn_alignbyte(R.phi, R.plo, csh);
+    }
+    const float sf = h16(pown), bf = h16(pown >> 16);
+    float mf = __builtin_rintf(-bf * __builtin_amdgcn_rcpf(sf));
+    mf = sf > 0.0f ? __builtin_fminf(__builtin_fmaxf(mf, 0.0f), kQ) : 0.0f;
+    const float cb = __builtin_fmaf(sf, mf, bf);
+    const float wl = R.w;
+    accb = first ? wl * cb : __builtin_fmaf(wl, cb, accb);
+    const uint32_t mi = (uint32_t)mf;
+    const uint32_t wsb = __builtin_bit_cast(uint32_t, wl * sf);
+    const uint32_t nlo = (0xE400u + mi) * 0x00010001u;       // fp16 -(1024 + m), twice
+    const uint32_t nhi = (0xE400u + 16u * mi) * 0x00010001u; // fp16 -(1024 + 16 m), twice
+#pragma unroll
+    for (int u = 0; u < SLOTS; ++u) {
+      if (u < U) {
+        const float ws = __builtin_bit_cast(float, bperm(baddr[u], wsb));
+        const uint32_t lo = bperm(baddr[u], nlo);
+        const uint32_t hi = BITS == 4 ? bperm(baddr[u], nhi) : 0u;
+        if (u == 0 && first) {
+          accumulate_centered<BITS, VEC, true>(acc, R.cc[u], ws, lo, hi, K);
+        } else {
+          accumulate_centered<BITS, VEC>(acc, R.cc[u], ws, lo, hi, K);
+        }
+      }
+    }
   };
-
-  Rows RA, RB;
-  // prologue: bag 0's first batch in flight, ids of bag 1 requested
-  Tab tc = table_of(bag0);
-  int64_t cp0 = lane_i64(lp0, 0), cp1 = lane_i64(lp1, 0);
-  int cn = batch_len(cp0, cp1);
-  {
-    IdxT id;
-    float wl;
-    fetch_ids(cp0, cn, id, wl);
-    put_meta(0, cn, id, wl, tc.n_t);
-    wave_sync_lds();
-    issue(RA, 0, tc);
-  }
-  IdxT nid;
-  float nw;
-  {
-    const bool has = nb > 1;
-    const int64_t q0 = has ? lane_i64(lp0, 1) : 0, q1 = has ? lane_i64(lp1, 1) : 0;
-    fetch_ids(q0, batch_len(q0, q1), nid, nw);
-  }
-
-  // one pipeline step: bag i (rows in Rc, metadata in buffer i&1) is
-  // finished while bag i+1's rows go out into Rn
-  auto step = [&](int i, Rows& Rc, Rows& Rn) {
-    const int cb = i & 1;
-    const bool has1 = i + 1 < nb, has2 = i + 2 < nb;
-    Tab tn = tc;
-    if (has1 && (bag0 + i + 1) / B != tc.t) tn = table_of(bag0 + i + 1);
-    const int64_t np0 = has1 ? lane_i64(lp0, i + 1) : 0;
-    const int64_t np1 = has1 ? lane_i64(lp1, i + 1) : 0;
-    const int nn = batch_len(np0, np1);
-    put_meta(cb ^ 1, nn, nid, nw, tn.n_t);
-    wave_sync_lds();
-    issue(Rn, cb ^ 1, tn);
-    {
-      const int64_t q0 = has2 ? lane_i64(lp0, i + 2) : 0;
-      const int64_t q1 = has2 ? lane_i64(lp1, i + 2) : 0;
-      fetch_ids(q0, batch_len(q0, q1), nid, nw);
+  // ---- consumer cursor: the bag whose sums are accumulating ----
+  int64_t ct = t0, cb = b0;
+  auto finish = [&]() {
+    float* o = out + (cb * T + ct) * (int64_t)dim;
+    if (++cb == B) {
+      cb = 0;
+      ++ct;
     }
-    float acc[EPL];
-    consume(Rc, cb, cn, tc, acc, true);
-    // ids past the first 64 of this bag (rare): synchronous batches
-    for (int64_t c0 = cp0 + kWave; c0 < cp1; c0 += kWave) {
-      const int n = batch_len(c0, cp1);
-      IdxT id;
-      float wl;
-      fetch_ids(c0, n, id, wl);
-      wave_sync_lds();
-      put_meta(cb, n, id, wl, tc.n_t);
-      wave_sync_lds();
-      issue(Rc, cb, tc);
-      consume(Rc, cb, n, tc, acc, false);
-    }
-    const int64_t bag = bag0 + i;
-    const int64_t b = bag - tc.t * B;
-    float* o = out + (b * T + tc.t) * (int64_t)dim;
+    const float bias = wave_sum(accb);
     if constexpr (LPR == 8) {
-      // 8 row groups: in-register reduce-scatter, one 8-byte store per lane
       float r0, r1;
       reduce_scatter_g8(acc, lane, r0, r1);
+      r0 = bag_empty ? 0.0f : r0 + bias;
+      r1 = bag_empty ? 0.0f : r1 + bias;
       const int e0 = s * 16 + ((lane >> 5) & 1) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 3) & 1) * 2;
-      if (e0 + 1 < dim) {
-        if ((dim & 1) == 0) {
-          *reinterpret_cast<float2*>(o + e0) = make_float2(r0, r1);
-        } else {
-          o[e0] = r0;
-          o[e0 + 1] = r1;
-        }
-      } else if (e0 < dim) {
-        o[e0] = r0;
+      if (dim == LPR * EPL) {
+        *reinterpret_cast<float2*>(o + e0) = make_float2(r0, r1);
+      } else {
+        if (e0 < dim) o[e0] = r0;
+        if (e0 + 1 < dim) o[e0 + 1] = r1;
       }
     } else {
-      float* rw = red[wv];
+      float* rw = red[LPR == 8 ? 0 : wv];
 #pragma unroll
       for (int e = 0; e < EPL; e += 4)
         *reinterpret_cast<float4*>(rw + g * (LPR * EPL) + s * EPL + e) =
@@ -1085,19 +1259,76 @@ __global__ __launch_bounds__(kBlock) void bag_pipe_kernel(
         float v = rw[e];
 #pragma unroll
         for (int gg = 1; gg < RG; ++gg) v += rw[gg * (LPR * EPL) + e];
-        o[e] = v;
+        o[e] = bag_empty ? 0.0f : v + bias;
       }
       wave_sync_lds();
     }
-    tc = tn;
-    cp0 = np0;
-    cp1 = np1;
-    cn = nn;
   };
 
-  for (int i = 0; i < nb; i += 2) {
-    step(i, RA, RB);
-    if (i + 1 < nb) step(i + 1, RB, RA);
+  // the pipelined batch loop; BUF: every table of the run is under kBufLimit
+  // bytes, so all rows go through descriptors (a wave-uniform choice made
+  // once, keeping the loop free of a per-batch branch between the two forms)
+  auto run = [&](auto BUF_) {
+    // ring buffers indexed by batch number mod NBUF: ids (and weights, and
+    // the batch's metadata) are requested DEPTH steps before the batch's rows
+    // are issued, and rows are consumed DEPTH steps after they are issued.
+    // Waiting for a batch's ids then leaves the DEPTH batches of rows issued
+    // after them in flight.
+    Rows R[NBUF];
+    int rnf[NBUF];  // id count | flags << 8 of the batch in rows buffer j
+    IdxT bid[NBUF];
+    float bw[NBUF];
+    Batch bi[NBUF];
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) bi[j] = next_batch(bid[j], bw[j]);
+    // step k (I = k mod NBUF): request the ids of batch k + DEPTH, issue the
+    // rows of batch k
+    auto produce_issue = [&](auto I_) {
+      constexpr int I = decltype(I_)::value, P = (I + NBUF - 1) % NBUF;
+      bi[P] = next_batch(bid[P], bw[P]);
+      use_table(bi[I].t);
+      issue(R[I], bi[I], bid[I], bw[I], BUF_);
+      rnf[I] = bi[I].n | (bi[I].f << 8);
+    };
+    // ... and consume batch k - DEPTH; false once every batch is consumed
+    auto step = [&](auto I_) {
+      constexpr int C = (decltype(I_)::value + 1) % NBUF;
+      produce_issue(I_);
+      consume(R[C], rnf[C]);
+      if (rnf[C] & (kLast << 8)) finish();
+      return (rnf[C] & (kReal << 8)) != 0;
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    produce_issue(I0{});
+    if constexpr (DEPTH == 1) {
+      while (step(I1{}) && step(I0{})) {
+      }
+    } else if constexpr (DEPTH == 2) {
+      produce_issue(I1{});
+      while (step(I2{}) && step(I0{}) && step(I1{})) {
+      }
+    } else {
+      produce_issue(I1{});
+      produce_issue(I2{});
+      while (step(I3{}) && step(I0{}) && step(I1{}) && step(I2{})) {
+      }
+    }
+  };
+  // tables of the run: t0 .. the table of its last bag
+  bool run_buf = true;
+  for (int64_t t = t0; t <= (bag0 + nb - 1) / B; ++t) {
+    const int64_t a0 = table_offsets[t], a1 = table_offsets[t + 1];
+    const bool ok = uniform_flag(a0 >= 0 && a1 > a0 && a1 <= total_rows);
+    run_buf = run_buf && uniform_flag((ok ? (a1 - a0) * S : 0) < (int64_t)kBufLimit);
+  }
+  if (run_buf) {
+    run(std::true_type{});
+  } else {
+    run(std::false_type{});
   }
   if (errs && err_count) atomicAdd(err_count, errs);
 }
@@ -1363,20 +1594,21 @@ int launch_bag_wave_t(const BagArgs& a, hipStream_t st) {
   return launched();
 }
 
-template <int BITS, int LPR, typename IdxT, bool PA4, bool WEIGHTED>
-int launch_bag_pipe_w(const BagArgs& a, hipStream_t st) {
+template <int BITS, int LPR, typename IdxT, bool PA4, bool WEIGHTED, bool PX>
+int launch_bag_stream_w(const BagArgs& a, hipStream_t st) {
   const int64_t blocks = (a.n_bags + kWPB * kWave - 1) / (kWPB * kWave);
   if (blocks > 0x7fffffff) return QEMB_E_UNSUPPORTED;
-  hipLaunchKernelGGL((bag_pipe_kernel<BITS, LPR, IdxT, PA4, WEIGHTED>), dim3((unsigned)blocks), dim3(kBlock), 0, st,
-                     a.packed, a.S, a.total_rows, a.table_offsets, a.T, a.B, a.dim, a.C, a.indices,
-                     a.offsets, a.nnz, a.weights, a.out, a.err_count, a.n_bags);
+  hipLaunchKernelGGL((bag_stream_kernel<BITS, LPR, IdxT, PA4, WEIGHTED, PX>), dim3((unsigned)blocks),
+                     dim3(kBlock), 0, st, a.packed, a.S, a.total_rows, a.table_offsets, a.T, a.B,
+                     a.dim, a.C, a.indices, a.offsets, a.nnz, a.weights, a.out, a.err_count,
+                     a.n_bags);
   return launched();
 }
 
-template <int BITS, int LPR, typename IdxT, bool PA4>
-int launch_bag_pipe_t(const BagArgs& a, hipStream_t st) {
-  return a.weights ? launch_bag_pipe_w<BITS, LPR, IdxT, PA4, true>(a, st)
-                   : launch_bag_pipe_w<BITS, LPR, IdxT, PA4, false>(a, st);
+template <int BITS, int LPR, typename IdxT, bool PA4, bool PX>
+int launch_bag_stream_t(const BagArgs& a, hipStream_t st) {
+  return a.weights ? launch_bag_stream_w<BITS, LPR, IdxT, PA4, true, PX>(a, st)
+                   : launch_bag_stream_w<BITS, LPR, IdxT, PA4, false, PX>(a, st);
 }
 
 template <int BITS, int LPR>
@@ -1386,12 +1618,18 @@ int launch_bag_wave(const BagArgs& a, hipStream_t st) {
 }
 
 template <int BITS, int LPR>
-int launch_bag_pipe(const BagArgs& a, hipStream_t st) {
+int launch_bag_stream(const BagArgs& a, hipStream_t st) {
+  constexpr int VEC = StreamGeo<BITS, LPR>::VEC;
+  if constexpr (VEC == 8) {
+    if (a.C == LPR * VEC)  // codes fill the lanes; the scale/bias follows the last lane's codes
+      return a.idx64 ? launch_bag_stream_t<BITS, LPR, int64_t, true, true>(a, st)
+                     : launch_bag_stream_t<BITS, LPR, int32_t, true, true>(a, st);
+  }
   if (a.C % 4 == 0)
-    return a.idx64 ? launch_bag_pipe_t<BITS, LPR, int64_t, true>(a, st)
-                   : launch_bag_pipe_t<BITS, LPR, int32_t, true>(a, st);
-  return a.idx64 ? launch_bag_pipe_t<BITS, LPR, int64_t, false>(a, st)
-                 : launch_bag_pipe_t<BITS, LPR, int32_t, false>(a, st);
+    return a.idx64 ? launch_bag_stream_t<BITS, LPR, int64_t, true, false>(a, st)
+                   : launch_bag_stream_t<BITS, LPR, int32_t, true, false>(a, st);
+  return a.idx64 ? launch_bag_stream_t<BITS, LPR, int64_t, false, false>(a, st)
+                 : launch_bag_stream_t<BITS, LPR, int32_t, false, false>(a, st);
 }
 
 template <int BITS>
@@ -1399,10 +1637,10 @@ int dispatch_wave(const BagArgs& a, hipStream_t st) {
   constexpr int VEC = WaveBag<BITS, 1>::VEC;
   const int lpr = next_pow2((a.C + VEC - 1) / VEC);
   switch (lpr) {
-    case 1: return launch_bag_pipe<BITS, 1>(a, st);
-    case 2: return launch_bag_pipe<BITS, 2>(a, st);
-    case 4: return launch_bag_pipe<BITS, 4>(a, st);
-    case 8: return launch_bag_pipe<BITS, 8>(a, st);
+    case 1: return launch_bag_stream<BITS, 1>(a, st);
+    case 2: return launch_bag_stream<BITS, 2>(a, st);
+    case 4: return launch_bag_stream<BITS, 4>(a, st);
+    case 8: return launch_bag_stream<BITS, 8>(a, st);
     case 16: return launch_bag_wave<BITS, 16>(a, st);
     case 32: return launch_bag_wave<BITS, 32>(a, st);
     default: return launch_bag_wave<BITS, 64>(a, st);

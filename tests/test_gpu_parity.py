@@ -214,6 +214,27 @@ def test_bag_dims_ragged_bags(q, dim, bits, weighted):
     assert np.all(got[empty] == 0) and not np.any(np.signbit(got[empty]))
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("dim", [16, 128])
+def test_bag_long_and_boundary_lengths(q, dim, bits):
+    """Bag lengths around the lookup's batch sizes (31..33, 63..65) and far
+    past them (500, 1000), between empty and one-id bags."""
+    g = np.random.default_rng(5500 + dim + bits)
+    T, B = 2, 12
+    rows = [700, 900]
+    x = special_rows(g, sum(rows), dim)
+    x[np.abs(x) > 100] = 1.0
+    packed = oracle.quantize_rowwise(x, bits)
+    lengths = np.array([0, 1, 500, 64, 65, 33, 31, 32, 1000, 2, 63, 0] * T)
+    offsets = np.concatenate([[0], np.cumsum(lengths)])
+    idx = np.concatenate([g.integers(0, rows[gb // B], size=lengths[gb]) for gb in range(T * B)])
+    bt = synth.Batch(idx.astype(np.int32), offsets.astype(np.int32), g.random(idx.size).astype(np.float32),
+                     np.concatenate([[0], np.cumsum(rows)]).astype(np.int64), B, T)
+    got, err, ref, absd, rerr = _run_bag(q, packed, bt, dim, bits, bt.weights)
+    assert err == rerr == 0
+    assert_pooled_close(got, ref, absd, "long bags dim %d" % dim)
+
+
 def test_bag_invalid_ids_and_offsets_are_skipped_and_counted(q):
     g = np.random.default_rng(6000)
     dim, bits, T, B = 64, 4, 4, 50
