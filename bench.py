@@ -31,6 +31,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 VALU_PEAK_OPS = 256 * 64 * 2.4e9  # lane-ops/s: 256 CUs x 64 lanes x 2.4 GHz (no packed fp32)
+HEADLINE_KERNEL = "bag_stream_kernel<4, 8, int, true, true, true>"
+KERNEL_SOURCE = os.path.join(ROOT, "int4_row_wise_amd", "csrc", "qemb.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "bag_stream_int4_multihot_counters.md")
 
 
 def log(msg: str) -> None:
@@ -58,6 +61,32 @@ def algorithmic_bag_bytes(nnz: int, n_bags: int, dim: int, bits: int, idx_bytes:
     row = (dim * bits + 7) // 8 + 4
     per = row + idx_bytes + (4 if weighted else 0)
     return nnz * per + (n_bags + 1) * idx_bytes + n_bags * dim * 4
+
+
+def source_sha256(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
+    counter reads for a plain device copy of known size), or None when the
+    summary is missing or was taken on a different kernel source."""
+    try:
+        text = open(COUNTERS).read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    end = text.find("```", start + 7)
+    rec = json.loads(text[start + 7:end])
+    if rec.get("source_sha256") != source_sha256(KERNEL_SOURCE):
+        return None
+    return 1024.0 * (rec["fetch_kib_per_dispatch"] * rec["fetch_scale"] +
+                     rec["write_kib_per_dispatch"] * rec["write_scale"])
 
 
 class Timer:
@@ -187,10 +216,11 @@ def quantizer_extras(q, synth, torch, dev, reps=3):
     res["dequantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3, "GBps": (in_b + out_b) / ms / 1e6,
                          "hbm_frac": (in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS}
     ms = timed(lambda: q.quantize_rowwise(x, 4, q.GREEDY, w.n_bins, w.n_steps, out=packed), 1)
-    # algorithmic lane-ops: 2K+1 candidate windows per row, each ~ 8 ops per
-    # element (sub, mul, rint, max, min, fma, sub, mul) + d-1 adds + ~40 ops of
-    # per-window setup (two IEEE divisions, fp16 round trips)
-    ops = rows * (2 * w.n_steps + 1) * (9 * dim + 40)
+    # algorithmic lane-ops: 2K+1 candidate windows per row, each 8 fp32
+    # operations per element (x - b, * 1/s, round, clamp, s*q + b, x - y,
+    # square, pairwise add); the per-window setup (two divisions, fp16
+    # round trips) is not counted
+    ops = rows * (2 * w.n_steps + 1) * (8 * dim)
     res["greedy_quantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3,
                               "valu_ops_per_s": ops / ms * 1e3,
                               "valu_frac": ops / ms * 1e3 / VALU_PEAK_OPS}
@@ -275,8 +305,9 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "bag_kernel<4,8,8,8,4>",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+            "traffic_unit": "bytes per launch (HBM, from FETCH_SIZE/WRITE_SIZE)",
+            "kernel": HEADLINE_KERNEL,
             "bytes_per_launch": bytes_timed / args.steps,
             "avg_launch_ms": avg_ms,
         },
