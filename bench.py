@@ -83,7 +83,9 @@ def measured_traffic():
         return None
     end = text.find("```", start + 7)
     rec = json.loads(text[start + 7:end])
-    if rec.get("source_sha256") != source_sha256(KERNEL_SOURCE):
+    from int4_row_wise_amd import build as qbuild
+    src = source_sha256(KERNEL_SOURCE)
+    if rec.get("source_sha256") != src or qbuild.built_source_sha256() != src:
         return None
     return 1024.0 * (rec["fetch_kib_per_dispatch"] * rec["fetch_scale"] +
                      rec["write_kib_per_dispatch"] * rec["write_scale"])
@@ -154,11 +156,11 @@ def bench_bags(q, torch, packed, toff, batches, w, bits, steps, warmup, out):
     return tm.ms(), wall
 
 
-def cpu_baseline(oracle, synth, torch, w, bits, batch0, dev, budget_s=20.0):
+def cpu_baseline(oracle, synth, torch, w, bits, batch0, dev, budget_s=15.0):
     """The oracle (plain C, OpenMP over bags) on the first tables of the
     workload: every bag of those tables, over the oracle's own packing of
     the same generated values.  Returns lookups/s over the sample."""
-    n_tab = 2
+    n_tab = 8
     xs = [synth.table_values_torch(w, t, 0, w.rows[t], dev).cpu().numpy() for t in range(n_tab)]
     x = np.concatenate(xs)
     del xs
@@ -171,18 +173,82 @@ def cpu_baseline(oracle, synth, torch, w, bits, batch0, dev, budget_s=20.0):
     wts = batch0["w_np"][:nnz]
     toff = np.array([0] + list(np.cumsum(w.rows[:n_tab])), dtype=np.int64)
     reps, t_total = 0, 0.0
-    while t_total < budget_s and reps < 20:
+    while t_total < budget_s and reps < 1000:
         t0 = time.perf_counter()
         oracle.bag_forward(packed, toff, B, w.dim, bits, idx, offs, wts)
         t_total += time.perf_counter() - t0
         reps += 1
+    threads = oracle.num_threads()
+    # one thread, one table (a shorter sample)
+    offs1 = offs[: B + 1]
+    n1 = int(offs1[-1])
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.bag_forward(packed, toff, B, w.dim, bits, idx[:n1], offs1, wts[:n1])
+        t1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(threads)
     return {
-        "value": nnz * reps / t_total, "unit": "lookups/s", "cores": oracle.num_threads(),
+        "value": nnz * reps / t_total, "unit": "lookups/s", "cores": threads,
         "kind": "oracle",
         "sample": "tables 0-%d of %d (all %d bags each, %d lookups), %d repetitions, oracle-packed "
                   "INT4 rows of the same generated values" % (n_tab - 1, w.n_tables, B, nnz, reps),
         "seconds": round(t_total, 2),
+        "one_thread_lookups_per_s": n1 / t1,
+        "affinity_cores": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def launch_stats(ms):
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean_ms": float(a.mean()), "median_ms": float(np.median(a)), "min_ms": float(a.min()),
+            "p90_ms": float(np.percentile(a, 90)), "launches": int(a.size)}
+
+
+def device_copy_gbps(torch, dev, nbytes=1 << 30, reps=10):
+    """Achievable bandwidth of a plain device-to-device copy on this GPU
+    (read + write bytes per second), for context next to the rooflines."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    b = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for _ in range(reps):
+        with tm:
+            b.copy_(a)
+    ms = float(np.median(tm.ms()))
+    del a, b
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def bench_cold(q, torch, packed, toff, batch, w, bits, out, dev, reps=5):
+    """Lookups with L2 and the MALL flushed first: each launch follows a
+    write of a 1 GiB scratch buffer (not timed)."""
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    ms = []
+    for _ in range(reps):
+        scratch.fill_(reps)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        with tm:
+            q.bag_forward(packed, toff, w.batch, w.dim, bits, batch["idx"], batch["offs"], batch["w"],
+                          out=out)
+        ms.extend(tm.ms())
+    del scratch
+    return ms
 
 
 def quantizer_extras(q, synth, torch, dev, reps=3):
@@ -252,6 +318,8 @@ def main():
     from int4_row_wise_amd import build as qbuild
     from int4_row_wise_amd import synth
     qbuild.ensure_built()
+    if qbuild.built_source_sha256() != qbuild.source_sha256():
+        log("warning: libqemb.so was not built from the current kernel source")
     q.load_library()
     dev = torch.device("cuda:0")
     w = synth.workload(4)
@@ -281,6 +349,7 @@ def main():
     achieved = bytes_timed / args.steps / (avg_ms * 1e-3) / 1e9
     log("INT4 bag forward: %.3f ms/launch (median %.3f), %.0f GB/s algorithmic" % (
         avg_ms, float(np.median(ms)), achieved))
+    stats = launch_stats(ms)
 
     result = {
         "metric": "pooled lookups/sec and achieved HBM GB/s (% of roofline), INT4 bag fwd",
@@ -311,6 +380,7 @@ def main():
             "bytes_per_launch": bytes_timed / args.steps,
             "avg_launch_ms": avg_ms,
         },
+        "launch_ms": stats,
     }
 
     if not args.no_extras:
@@ -334,6 +404,13 @@ def main():
             "GBps": bb / (np.mean(msu) * 1e-3) / 1e9,
             "hbm_frac": bb / (np.mean(msu) * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del ub
+        b0 = algorithmic_bag_bytes(batches[0]["nnz"], n_bags, w.dim, 4, 4, True)
+        msc = bench_cold(q, torch, packed[4], toff, batches[0], w, 4, out, dev)
+        result["cold_cache"] = {
+            "note": "each launch after writing a 1 GiB scratch buffer (L2 and MALL flushed)",
+            "launch_ms": launch_stats(msc), "GBps": b0 / (np.median(msc) * 1e-3) / 1e9,
+            "hbm_frac": b0 / (np.median(msc) * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        result["device_copy_GBps"] = device_copy_gbps(torch, dev)
         del packed[8]
         torch.cuda.empty_cache()
         t0 = time.time()

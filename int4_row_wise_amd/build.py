@@ -17,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "qemb.hip")
 HEADER = os.path.join(ROOT, "include", "qemb.h")
 LIB = os.path.join(HERE, "libqemb.so")
+LIB_HASH = LIB + ".srchash"  # source sha256 recorded at build time
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
@@ -48,7 +49,25 @@ def build(force: bool = True, verbose: bool = False) -> str:
     if out.strip() and verbose:
         print(out)
     os.replace(tmp, LIB)
+    with open(LIB_HASH, "w") as f:
+        f.write(source_sha256() + "\n")
     return LIB
+
+
+def source_sha256() -> str:
+    """sha256 of the kernel source the library is built from."""
+    import hashlib
+    with open(SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def built_source_sha256() -> str | None:
+    """The source hash recorded when libqemb.so was last built, if any."""
+    try:
+        with open(LIB_HASH) as f:
+            return f.read().strip()
+    except OSError:
+        return None
 
 
 def ensure_built() -> str:
