@@ -16,7 +16,9 @@ pages it follows, is stated in the C source:
 * the pooled embedding-bag lookup ("Deep Learning Recommendation Model for
   Personalization and Recommendation Systems", review page, "Proposed
   method"), summed in binary64;
-* the normalized l2 error (Post-Training 4-bit page, "Proposed method").
+* the normalized l2 error (Post-Training 4-bit page, "Proposed method");
+* codebook rows: 16 fp32 levels per row from 1-D k-means and 4-bit codes
+  (Post-Training 4-bit page, "Proposed method" and "Main findings").
 """
 from __future__ import annotations
 
@@ -79,6 +81,17 @@ def lib() -> ctypes.CDLL:
         L.oracle_bag_forward.restype = i32
         L.oracle_l2_error.argtypes = [p, p, i64, i32, i32, p]
         L.oracle_l2_error.restype = i32
+        L.oracle_codebook_row_stride.argtypes = [i32]
+        L.oracle_codebook_row_stride.restype = i64
+        L.oracle_quantize_codebook.argtypes = [p, i64, i32, i32, p]
+        L.oracle_quantize_codebook.restype = i32
+        L.oracle_dequantize_codebook.argtypes = [p, i64, i32, p]
+        L.oracle_dequantize_codebook.restype = i32
+        L.oracle_bag_forward_codebook.argtypes = [p, i64, p, i32, i64, i32, p, p, i64,
+                                                  i32, i32, p, p, p, p]
+        L.oracle_bag_forward_codebook.restype = i32
+        L.oracle_l2_error_codebook.argtypes = [p, p, i64, i32, p]
+        L.oracle_l2_error_codebook.restype = i32
         _lib = L
     return _lib
 
@@ -193,6 +206,95 @@ def l2_error(x: np.ndarray, packed: np.ndarray, bits: int) -> dict:
     rc = lib().oracle_l2_error(_ptr(x), _ptr(packed), rows, dim, bits, _ptr(out))
     if rc != 0:
         raise OracleError("oracle_l2_error returned %d" % rc)
+    frob = float(np.sqrt(out[2] / out[3])) if out[3] > 0 else 0.0
+    return {"mean_row": float(out[0]), "rows": int(out[1]), "sum_err2": float(out[2]),
+            "sum_x2": float(out[3]), "frobenius": frob}
+
+
+# ---- codebook rows (16 fp32 levels per row from k-means, 4-bit codes) ----
+
+CODEBOOK_ITERS = 10  # default Lloyd iterations
+
+
+def codebook_row_stride(dim: int) -> int:
+    return int(lib().oracle_codebook_row_stride(dim))
+
+
+def quantize_codebook(x: np.ndarray, n_iter: int = CODEBOOK_ITERS) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, dim = x.shape
+    packed = np.empty((rows, codebook_row_stride(dim)), dtype=np.uint8)
+    rc = lib().oracle_quantize_codebook(_ptr(x), rows, dim, n_iter, _ptr(packed))
+    if rc != 0:
+        raise OracleError("oracle_quantize_codebook returned %d" % rc)
+    return packed
+
+
+def codebook_levels(packed: np.ndarray) -> np.ndarray:
+    """The 16 fp32 levels of each codebook row ([rows, 16])."""
+    return np.ascontiguousarray(packed[:, :64]).view("<f4").reshape(-1, 16)
+
+
+def codebook_codes(packed: np.ndarray, dim: int) -> np.ndarray:
+    """The 4-bit codes of each codebook row ([rows, dim])."""
+    b = packed[:, 64:64 + (dim + 1) // 2]
+    codes = np.empty((packed.shape[0], 2 * b.shape[1]), dtype=np.uint8)
+    codes[:, 0::2] = b & 15
+    codes[:, 1::2] = b >> 4
+    return codes[:, :dim]
+
+
+def dequantize_codebook(packed: np.ndarray, dim: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    y = np.empty((rows, dim), dtype=np.float32)
+    rc = lib().oracle_dequantize_codebook(_ptr(packed), rows, dim, _ptr(y))
+    if rc != 0:
+        raise OracleError("oracle_dequantize_codebook returned %d" % rc)
+    return y
+
+
+def bag_forward_codebook(packed: np.ndarray, table_offsets: np.ndarray, B: int, dim: int,
+                         indices: np.ndarray, offsets: np.ndarray, weights: np.ndarray | None = None,
+                         pool_mode: int | None = None, total_rows: int | None = None):
+    """Returns (out[B, T, dim] float64, abs_terms[B, T, dim] float64, err_count)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    table_offsets = np.ascontiguousarray(table_offsets, dtype=np.int64)
+    T = table_offsets.size - 1
+    if indices.dtype == np.int32:
+        itype = 0
+    elif indices.dtype == np.int64:
+        itype = 1
+    else:
+        raise TypeError("indices must be int32 or int64")
+    indices = np.ascontiguousarray(indices)
+    offsets = np.ascontiguousarray(offsets, dtype=indices.dtype)
+    if pool_mode is None:
+        pool_mode = SUM if weights is None else WEIGHTED_SUM
+    if weights is not None:
+        weights = np.ascontiguousarray(weights, dtype=np.float32)
+    if total_rows is None:
+        total_rows = packed.shape[0]
+    out = np.empty((B, T, dim), dtype=np.float64)
+    absd = np.empty((B, T, dim), dtype=np.float64)
+    err = np.zeros(1, dtype=np.int64)
+    rc = lib().oracle_bag_forward_codebook(_ptr(packed), total_rows, _ptr(table_offsets), T, B, dim,
+                                           _ptr(indices), _ptr(offsets), indices.size, itype,
+                                           pool_mode, _ptr(weights), _ptr(out), _ptr(absd),
+                                           _ptr(err))
+    if rc != 0:
+        raise OracleError("oracle_bag_forward_codebook returned %d" % rc)
+    return out, absd, int(err[0])
+
+
+def l2_error_codebook(x: np.ndarray, packed: np.ndarray) -> dict:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    rows, dim = x.shape
+    out = np.zeros(4, dtype=np.float64)
+    rc = lib().oracle_l2_error_codebook(_ptr(x), _ptr(packed), rows, dim, _ptr(out))
+    if rc != 0:
+        raise OracleError("oracle_l2_error_codebook returned %d" % rc)
     frob = float(np.sqrt(out[2] / out[3])) if out[3] > 0 else 0.0
     return {"mean_row": float(out[0]), "rows": int(out[1]), "sum_err2": float(out[2]),
             "sum_x2": float(out[3]), "frobenius": frob}

@@ -176,3 +176,46 @@ def encode(x, bits, clip="range", n_bins=200, n_steps=100):
     row[C:C + 2] = [s16 & 0xFF, s16 >> 8]
     row[C + 2:C + 4] = [b16 & 0xFF, b16 >> 8]
     return row
+
+
+# ---- codebook rows: 16 levels from 1-D k-means (Lloyd), 4-bit codes ----
+
+def codebook(x, n_iter=10):
+    """(levels[16] float32, codes[d]) by the codebook rule: start at the
+    row's uniform grid, n_iter rounds of nearest-level assignment (lowest
+    index on ties) and member means (pairwise member sum / count), then the
+    final assignment."""
+    x = np.asarray(x, dtype=np.float32)
+    lo, hi = row_range(x)
+    delta = (F32(hi) - F32(lo)) / F32(15)
+    c = np.array([fma32(F32(k), delta, lo) + F32(0.0) for k in range(16)], dtype=np.float32)
+
+    def assign(c):
+        dist = np.abs((x[:, None] - c[None, :]).astype(np.float32))
+        return np.argmin(dist, axis=1)  # first minimum: lowest index on ties
+
+    for _ in range(n_iter):
+        a = assign(c)
+        nxt = c.copy()
+        for k in range(16):
+            m = a == k
+            if m.any():
+                v = np.where(m, x, F32(0.0)).astype(np.float32)
+                nxt[k] = F32(pairwise(v) / F32(int(m.sum()))) + F32(0.0)
+        c = nxt
+    return c, assign(c)
+
+
+def encode_codebook(x, n_iter=10):
+    """Packed codebook row bytes (16 levels fp32 LE | codes | zero pad to 16 B)."""
+    x = np.asarray(x, dtype=np.float32)
+    c, q = codebook(x, n_iter)
+    d = x.size
+    C = (d + 1) // 2
+    S = (64 + C + 15) // 16 * 16
+    row = np.zeros(S, dtype=np.uint8)
+    row[:64] = np.frombuffer(c.astype("<f4").tobytes(), dtype=np.uint8)
+    qq = np.zeros(2 * C, dtype=np.int64)
+    qq[:d] = q
+    row[64:64 + C] = (qq[0::2] | (qq[1::2] << 4)).astype(np.uint8)
+    return row
