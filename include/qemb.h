@@ -177,6 +177,61 @@ size_t qemb_l2_error_workspace_bytes(void);
 int qemb_l2_error(const float* x, const uint8_t* packed, int64_t rows, int32_t dim,
                   int32_t bits, void* workspace, double* out4, qemb_stream_t stream);
 
+/*
+ * Codebook rows ("Post-Training 4-bit Quantization on Embedding Tables",
+ * review page, "Proposed method": per-row codebook quantization by k-means
+ * clustering with 4-bit codes; "Main findings": 18.8%-37.5% of the fp32
+ * size).  A row is 16 fp32 levels (64 bytes, little-endian) followed by
+ * ceil(dim/2) code bytes (element 2k in the low nibble of byte 64 + k) and
+ * zero padding to a multiple of 16 bytes.
+ */
+
+/* Codebook row stride in bytes: 16 * ceil((64 + ceil(dim/2)) / 16), or -1 if
+ * dim < 1 or dim > QEMB_MAX_DIM. */
+int64_t qemb_codebook_row_stride(int32_t dim);
+
+/*
+ * Per-row 1-D k-means codebook quantization (same passage):
+ *   levels start on the row's uniform grid c_k = fmaf(k, (max-min)/15, min)
+ *   (+0, fp32); then n_iter rounds of: assign every element to its nearest
+ *   level (smallest k on ties), and move every level that has members to
+ *   their mean (pairwise sum of the member values, +0 for the other elements,
+ *   over the row padded with +0 to a power of two, divided by the member
+ *   count, fp32); levels without members stay.  The codes are the nearest
+ *   levels after the last round.  Results are bit-exact and deterministic.
+ *   x       [rows][dim] fp32, 16-byte aligned (finite values)
+ *   rows    >= 0 (0 = nothing to do);  dim 1 .. QEMB_MAX_DIM
+ *   n_iter  >= 0 rounds (0 = the uniform grid)
+ *   packed  [rows][qemb_codebook_row_stride(dim)] bytes, 16-byte aligned,
+ *           written in full
+ */
+int qemb_quantize_codebook(const float* x, int64_t rows, int32_t dim, int32_t n_iter,
+                           uint8_t* packed, qemb_stream_t stream);
+
+/* Decode codebook rows: y[r][k] = level_r[code_rk] (exact copies).
+ *   packed [rows][S] and y [rows][dim] fp32, both 16-byte aligned. */
+int qemb_dequantize_codebook(const uint8_t* packed, int64_t rows, int32_t dim, float* y,
+                             qemb_stream_t stream);
+
+/*
+ * Fused decode + pooled embedding-bag lookup over codebook rows: the same
+ * arguments, output, accumulation and error handling as qemb_bag_forward,
+ * with `packed` holding codebook rows (stride qemb_codebook_row_stride(dim))
+ * and no `bits` argument.
+ */
+int qemb_bag_forward_codebook(const uint8_t* packed, int64_t total_rows,
+                              const int64_t* table_offsets, int32_t T, int64_t B, int32_t dim,
+                              const void* indices, const void* offsets, int64_t nnz,
+                              int32_t index_type, int32_t pool_mode, const float* weights,
+                              float* out, int32_t* err_count, qemb_stream_t stream);
+
+/*
+ * Normalized l2 error of codebook rows against their fp32 source: the same
+ * four binary64 results, workspace and alignment as qemb_l2_error.
+ */
+int qemb_l2_error_codebook(const float* x, const uint8_t* packed, int64_t rows, int32_t dim,
+                           void* workspace, double* out4, qemb_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1407,6 +1407,304 @@ __global__ __launch_bounds__(kBlock) void l2_final_kernel(const double* __restri
 }
 
 // ---------------------------------------------------------------------------
+// codebook rows: 16 fp32 levels per row (1-D k-means), 4-bit codes
+// ("Post-Training 4-bit Quantization on Embedding Tables", review page,
+// "Proposed method": codebook quantization by k-means clustering; "Main
+// findings": 18.8%-37.5% of the fp32 size, lowest normalized l2 loss).
+// Row: levels c_0..c_15 (64 bytes) | codes (element 2k in the low nibble of
+// byte 64 + k) | zero padding to a multiple of 16 bytes.
+// ---------------------------------------------------------------------------
+
+constexpr int kCbLevels = 16;
+
+// smallest k minimizing |x - c_k| (one fp32 subtraction each, exact |.|)
+__device__ __forceinline__ int nearest_level(float x, const float (&c)[kCbLevels]) {
+  int best = 0;
+  float bd = __builtin_fabsf(x - c[0]);
+#pragma unroll
+  for (int k = 1; k < kCbLevels; ++k) {
+    const float dk = __builtin_fabsf(x - c[k]);
+    const bool b = dk < bd;
+    bd = b ? dk : bd;
+    best = b ? k : best;
+  }
+  return best;
+}
+
+// LPR lanes per row, lane s holding the contiguous elements [s*EPL,
+// (s+1)*EPL) of the row padded with +0 to P = EPL*LPR (a power of two), so a
+// lane's pairwise sum of its chunk followed by xor butterflies over the LPR
+// lanes is the contiguous-halves pairwise sum of the padded row.
+//   1. levels start on the row's uniform grid c_k = fma(k, (hi-lo)/15, lo) + 0;
+//   2. n_iter times: nearest level of every element; every level with
+//      members becomes (pairwise sum of the members' values, +0 elsewhere) /
+//      member count + 0; a level without members keeps its value;
+//   3. codes: nearest level with the final levels.
+template <int EPL, int LPR>
+__global__ __launch_bounds__(kBlock) void quantize_codebook_kernel(
+    const float* __restrict__ x, int64_t rows, int dim, int S, int vec4, int n_iter,
+    uint8_t* __restrict__ packed) {
+  const int s = threadIdx.x % LPR;
+  const int64_t groups = (int64_t)gridDim.x * (kBlock / LPR);
+  for (int64_t row = (int64_t)blockIdx.x * (kBlock / LPR) + threadIdx.x / LPR; row < rows;
+       row += groups) {
+    const float* xr = x + row * dim;
+    const int e0 = s * EPL;
+    const int valid = min(max(dim - e0, 0), EPL);
+    float v[EPL];
+    if (EPL >= 4 && vec4 && valid == EPL) {
+#pragma unroll
+      for (int k = 0; k < EPL; k += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(xr + e0 + k);
+        v[k] = a.x; v[k + 1] = a.y; v[k + 2] = a.z; v[k + 3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) v[k] = (k < valid) ? xr[e0 + k] : 0.0f;
+    }
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      if (k < valid) {
+        mn = fminf(mn, v[k]);
+        mx = fmaxf(mx, v[k]);
+      }
+    }
+    const float lo = group_min<LPR>(mn) + 0.0f;
+    const float hi = group_max<LPR>(mx) + 0.0f;
+    const float delta = (hi - lo) / (float)(kCbLevels - 1);
+    float c[kCbLevels];
+#pragma unroll
+    for (int k = 0; k < kCbLevels; ++k) c[k] = __builtin_fmaf((float)k, delta, lo) + 0.0f;
+    int a[EPL];
+    for (int it = 0; it < n_iter; ++it) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a[e] = e < valid ? nearest_level(v[e], c) : -1;
+      float nx[kCbLevels];
+#pragma unroll
+      for (int k = 0; k < kCbLevels; ++k) {
+        float u[EPL];
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const bool m = a[e] == k;
+          u[e] = m ? v[e] : 0.0f;
+          cnt += m ? 1 : 0;
+        }
+#pragma unroll
+        for (int h = 1; h < EPL; h <<= 1) {
+#pragma unroll
+          for (int e = 0; e < EPL; e += 2 * h) u[e] = u[e] + u[e + h];
+        }
+        float tot = u[0];
+#pragma unroll
+        for (int m = 1; m < LPR; m <<= 1) {
+          tot = tot + __shfl_xor(tot, m);
+          cnt += __shfl_xor(cnt, m);
+        }
+        nx[k] = cnt > 0 ? tot / (float)cnt + 0.0f : c[k];
+      }
+#pragma unroll
+      for (int k = 0; k < kCbLevels; ++k) c[k] = nx[k];
+    }
+    // codes of this lane's elements (padding elements code 0)
+    uint32_t cw[(EPL + 7) / 8];
+#pragma unroll
+    for (int j = 0; j < (EPL + 7) / 8; ++j) cw[j] = 0u;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      if (e < valid) cw[e / 8] |= (uint32_t)nearest_level(v[e], c) << (4 * (e % 8));
+    uint8_t* prow = packed + row * (int64_t)S;
+    // levels: 4 units of 16 bytes, round robin over the row's lanes
+#pragma unroll
+    for (int U = 0; U < 4; ++U)
+      if (U % LPR == s)
+        *reinterpret_cast<float4*>(prow + 16 * U) =
+            make_float4(c[4 * U], c[4 * U + 1], c[4 * U + 2], c[4 * U + 3]);
+    if constexpr (LPR >= 2) {
+      // EPL == 16: this lane's 8 code bytes at 64 + 8s (the lanes cover
+      // every byte from 64 to the stride; lanes past it store nothing)
+      if (64 + 8 * s < S) *reinterpret_cast<uint2*>(prow + 64 + 8 * s) = make_uint2(cw[0], cw[1]);
+    } else {
+      // one lane per row: codes (at most 8 bytes) and padding, 16-byte units
+      for (int U = 4; 16 * U < S; ++U)
+        *reinterpret_cast<uint4*>(prow + 16 * U) =
+            make_uint4(U == 4 ? cw[0] : 0u, U == 4 && EPL > 8 ? cw[(EPL + 7) / 8 - 1] : 0u, 0u, 0u);
+    }
+  }
+}
+
+// Dequantize codebook rows: groups of 16 lanes per row, lane k holding level
+// k; element codes are resolved by ds_bpermute from the group's lanes.  Every
+// lane of a wave runs the same number of passes (rows past the end are
+// clamped and not stored), so the cross-lane reads see all lanes active.
+__global__ __launch_bounds__(kBlock) void dequant_codebook_kernel(
+    const uint8_t* __restrict__ packed, int64_t rows, int dim, int S, float* __restrict__ y) {
+  const int lane = threadIdx.x % kWave;
+  const int k = lane % kCbLevels, gbase = lane - k;
+  const int64_t gpb = kBlock / kCbLevels;  // row groups per block
+  const int64_t stride_rows = (int64_t)gridDim.x * gpb;
+  const int64_t first = (int64_t)blockIdx.x * gpb + threadIdx.x / kCbLevels;
+  const int64_t nrounds = (rows + stride_rows - 1) / stride_rows;
+  const int npass = (dim + 127) / 128;  // 16 lanes x 8 elements per pass
+  for (int64_t rd = 0; rd < nrounds; ++rd) {
+    const int64_t row = first + rd * stride_rows;
+    const bool live = row < rows;
+    const uint8_t* prow = packed + (live ? row : 0) * (int64_t)S;
+    const float lv = *reinterpret_cast<const float*>(prow + 4 * k);
+    for (int pss = 0; pss < npass; ++pss) {
+      const int e0 = pss * 128 + 8 * k;
+      const uint32_t cwd = e0 < dim ? *reinterpret_cast<const uint32_t*>(prow + 64 + e0 / 2) : 0u;
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        o[j] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                             (gbase + (int)((cwd >> (4 * j)) & 15u)) * 4,
+                                             __builtin_bit_cast(int, lv)));
+      if (live && e0 < dim) {
+        float* yr = y + row * dim + e0;
+        if (e0 + 8 <= dim && (dim % 4) == 0) {
+          *reinterpret_cast<float4*>(yr) = make_float4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<float4*>(yr + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (e0 + j < dim) yr[j] = o[j];
+        }
+      }
+    }
+  }
+}
+
+// Pooled lookup over codebook rows: one wave per bag, 4 row groups of 16
+// lanes (lane k of a group holds level k of the group's current row and the
+// codes of 8 elements per 128-element pass); U rows per group in flight.
+// The groups' partial sums are added by xor shuffles across 16 and 32.
+template <typename IdxT, int NP, int U>
+__global__ __launch_bounds__(kBlock) void bag_codebook_kernel(
+    const uint8_t* __restrict__ packed, int64_t S, int64_t total_rows,
+    const int64_t* __restrict__ table_offsets, int T, int64_t B, int dim,
+    const void* __restrict__ indices, const void* __restrict__ offsets, int64_t nnz,
+    const float* __restrict__ weights, float* __restrict__ out, int32_t* __restrict__ err_count,
+    int64_t n_bags) {
+  const int lane = threadIdx.x % kWave;
+  const int k = lane % kCbLevels, gbase = lane - k, grp = lane / kCbLevels;
+  const int64_t bag = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
+  if (bag >= n_bags) return;
+  const int64_t t = bag / B, b = bag - t * B;
+  int errs = 0;
+  int64_t p0 = load_index<IdxT>(offsets, bag), p1 = load_index<IdxT>(offsets, bag + 1);
+  if (!(p0 >= 0 && p1 >= p0 && p1 <= nnz)) {
+    errs = lane == 0 ? 1 : 0;
+    p0 = p1 = 0;
+  }
+  const int64_t a0 = table_offsets[t], a1 = table_offsets[t + 1];
+  const bool tab_ok = a0 >= 0 && a1 > a0 && a1 <= total_rows;
+  const int64_t nt = tab_ok ? a1 - a0 : 0;
+  const uint8_t* base = packed + (tab_ok ? a0 : 0) * S;
+  const IdxT* ids = reinterpret_cast<const IdxT*>(indices);
+  if (total_rows == 0) {
+    // no row to read: every id is skipped and counted
+    errs += lane == 0 ? (int)(p1 - p0) : 0;
+    p1 = p0;
+  }
+  float acc[NP][8];
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[pp][j] = 0.0f;
+  for (int64_t q = p0; q < p1; q += 4 * U) {
+    float lv[U], wl[U];
+    uint32_t cwd[U][NP];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t pos = q + u * 4 + grp;
+      const bool in = pos < p1;
+      const int64_t id = in ? (int64_t)ids[pos] : 0;
+      const bool ok = in && id >= 0 && id < nt;
+      errs += (in && !ok && k == 0) ? 1 : 0;
+      const uint8_t* prow = base + (ok ? id : 0) * S;
+      wl[u] = ok ? (weights ? weights[pos] : 1.0f) : 0.0f;
+      lv[u] = *reinterpret_cast<const float*>(prow + 4 * k);
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const int e0 = pp * 128 + 8 * k;
+        cwd[u][pp] = e0 < dim ? *reinterpret_cast<const uint32_t*>(prow + 64 + e0 / 2) : 0u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float yv = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                          (gbase + (int)((cwd[u][pp] >> (4 * j)) & 15u)) * 4,
+                                                          __builtin_bit_cast(int, lv[u])));
+          acc[pp][j] = __builtin_fmaf(wl[u], yv, acc[pp][j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      acc[pp][j] += __shfl_xor(acc[pp][j], 16);
+      acc[pp][j] += __shfl_xor(acc[pp][j], 32);
+    }
+  if (grp == 0) {
+    float* o = out + (b * T + t) * (int64_t)dim;
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const int e0 = pp * 128 + 8 * k;
+      if (e0 + 8 <= dim && (dim % 4) == 0) {
+        *reinterpret_cast<float4*>(o + e0) = make_float4(acc[pp][0], acc[pp][1], acc[pp][2], acc[pp][3]);
+        *reinterpret_cast<float4*>(o + e0 + 4) = make_float4(acc[pp][4], acc[pp][5], acc[pp][6], acc[pp][7]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (e0 + j < dim) o[e0 + j] = acc[pp][j];
+      }
+    }
+  }
+  for (int m = 1; m < kWave; m <<= 1) errs += __shfl_xor(errs, m);
+  if (lane == 0 && errs && err_count) atomicAdd(err_count, errs);
+}
+
+__global__ __launch_bounds__(kBlock) void l2_partial_codebook_kernel(
+    const float* __restrict__ x, const uint8_t* __restrict__ packed, int64_t rows, int dim, int S,
+    double* __restrict__ part) {
+  __shared__ double sh[4 * kBlock];
+  double a[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int64_t row = (int64_t)blockIdx.x * kBlock + threadIdx.x; row < rows;
+       row += (int64_t)gridDim.x * kBlock) {
+    const float* xr = x + row * dim;
+    const uint8_t* prow = packed + row * (int64_t)S;
+    const float* lv = reinterpret_cast<const float*>(prow);
+    double e2 = 0.0, x2 = 0.0;
+    for (int e = 0; e < dim; ++e) {
+      const uint32_t q = (prow[64 + (e >> 1)] >> ((e & 1) * 4)) & 15u;
+      const double xk = (double)xr[e];
+      const double d = xk - (double)lv[q];
+      e2 += d * d;
+      x2 += xk * xk;
+    }
+    a[2] += e2;
+    a[3] += x2;
+    if (x2 > 0.0) {
+      a[0] += sqrt(e2) / sqrt(x2);
+      a[1] += 1.0;
+    }
+  }
+  block_sum4(a, sh);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) part[4 * blockIdx.x + c] = sh[c * kBlock];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------
 
@@ -1653,6 +1951,34 @@ int dispatch_wave(const BagArgs& a, hipStream_t st) {
 // C ABI
 // ---------------------------------------------------------------------------
 
+template <int EPL, int LPR>
+int launch_codebook(const float* x, int64_t rows, int dim, int S, int vec4, int n_iter,
+                    uint8_t* packed, hipStream_t st) {
+  hipLaunchKernelGGL((quantize_codebook_kernel<EPL, LPR>),
+                     dim3(grid_for(rows, kBlock / LPR, kGridCap)), dim3(kBlock), 0, st, x, rows, dim,
+                     S, vec4, n_iter, packed);
+  return launched();
+}
+
+// P = next power of two >= dim: one lane per row up to 16 elements, else
+// 16 elements per lane and P/16 lanes per row
+int dispatch_codebook(const float* x, int64_t rows, int dim, int S, int vec4, int n_iter,
+                      uint8_t* packed, hipStream_t st) {
+  switch (next_pow2(dim)) {
+    case 1: return launch_codebook<1, 1>(x, rows, dim, S, vec4, n_iter, packed, st);
+    case 2: return launch_codebook<2, 1>(x, rows, dim, S, vec4, n_iter, packed, st);
+    case 4: return launch_codebook<4, 1>(x, rows, dim, S, vec4, n_iter, packed, st);
+    case 8: return launch_codebook<8, 1>(x, rows, dim, S, vec4, n_iter, packed, st);
+    case 16: return launch_codebook<16, 1>(x, rows, dim, S, vec4, n_iter, packed, st);
+    case 32: return launch_codebook<16, 2>(x, rows, dim, S, vec4, n_iter, packed, st);
+    case 64: return launch_codebook<16, 4>(x, rows, dim, S, vec4, n_iter, packed, st);
+    case 128: return launch_codebook<16, 8>(x, rows, dim, S, vec4, n_iter, packed, st);
+    case 256: return launch_codebook<16, 16>(x, rows, dim, S, vec4, n_iter, packed, st);
+    case 512: return launch_codebook<16, 32>(x, rows, dim, S, vec4, n_iter, packed, st);
+    default: return launch_codebook<16, 64>(x, rows, dim, S, vec4, n_iter, packed, st);
+  }
+}
+
 extern "C" {
 
 int qemb_abi_version(void) { return QEMB_ABI_VERSION; }
@@ -1762,6 +2088,95 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
 }
 
 size_t qemb_l2_error_workspace_bytes(void) { return (size_t)kL2Blocks * 4 * sizeof(double); }
+
+int64_t qemb_codebook_row_stride(int32_t dim) {
+  if (dim < 1 || dim > QEMB_MAX_DIM) return -1;
+  return (64 + ((int64_t)dim + 1) / 2 + 15) / 16 * 16;
+}
+
+int qemb_quantize_codebook(const float* x, int64_t rows, int32_t dim, int32_t n_iter,
+                           uint8_t* packed, qemb_stream_t stream) {
+  if (rows < 0 || dim < 1 || n_iter < 0) return QEMB_E_INVALID_ARG;
+  if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
+  if (rows == 0) return QEMB_OK;
+  if (!x || !packed) return QEMB_E_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(packed)) return QEMB_E_MISALIGNED;
+  return dispatch_codebook(x, rows, dim, (int)qemb_codebook_row_stride(dim), dim % 4 == 0, n_iter,
+                           packed, reinterpret_cast<hipStream_t>(stream));
+}
+
+int qemb_dequantize_codebook(const uint8_t* packed, int64_t rows, int32_t dim, float* y,
+                             qemb_stream_t stream) {
+  if (rows < 0 || dim < 1) return QEMB_E_INVALID_ARG;
+  if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
+  if (rows == 0) return QEMB_OK;
+  if (!packed || !y) return QEMB_E_INVALID_ARG;
+  if (!aligned16(packed) || !aligned16(y)) return QEMB_E_MISALIGNED;
+  constexpr int kRowsPerBlock = kBlock / kCbLevels;
+  hipLaunchKernelGGL(dequant_codebook_kernel, dim3(grid_for(rows, kRowsPerBlock, kGridCap)),
+                     dim3(kBlock), 0, reinterpret_cast<hipStream_t>(stream), packed, rows, dim,
+                     (int)qemb_codebook_row_stride(dim), y);
+  return launched();
+}
+
+int qemb_bag_forward_codebook(const uint8_t* packed, int64_t total_rows,
+                              const int64_t* table_offsets, int32_t T, int64_t B, int32_t dim,
+                              const void* indices, const void* offsets, int64_t nnz,
+                              int32_t index_type, int32_t pool_mode, const float* weights,
+                              float* out, int32_t* err_count, qemb_stream_t stream) {
+  if (T < 0 || B < 0 || dim < 1 || total_rows < 0 || nnz < 0) return QEMB_E_INVALID_ARG;
+  if (index_type != QEMB_INDEX_INT32 && index_type != QEMB_INDEX_INT64) return QEMB_E_INVALID_ARG;
+  if (pool_mode != QEMB_POOL_SUM && pool_mode != QEMB_POOL_WEIGHTED_SUM) return QEMB_E_INVALID_ARG;
+  if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
+  if (T == 0 || B == 0) return QEMB_OK;
+  if (B > INT64_MAX / T) return QEMB_E_INVALID_ARG;
+  if (!table_offsets || !offsets || !out) return QEMB_E_INVALID_ARG;
+  if (nnz > 0 && !indices) return QEMB_E_INVALID_ARG;
+  if (total_rows > 0 && !packed) return QEMB_E_INVALID_ARG;
+  if (pool_mode == QEMB_POOL_WEIGHTED_SUM && nnz > 0 && !weights) return QEMB_E_INVALID_ARG;
+  if ((packed && !aligned16(packed)) || !aligned16(out)) return QEMB_E_MISALIGNED;
+  const int64_t n_bags = (int64_t)T * B;
+  const int64_t blocks = (n_bags + kWPB - 1) / kWPB;
+  if (blocks > 0x7fffffff) return QEMB_E_UNSUPPORTED;
+  const float* w = pool_mode == QEMB_POOL_WEIGHTED_SUM ? weights : nullptr;
+  const int64_t S = qemb_codebook_row_stride(dim);
+  const int np = (dim + 127) / 128;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  auto go = [&](auto idx_tag, auto np_tag) {
+    using IdxT = decltype(idx_tag);
+    constexpr int NP = decltype(np_tag)::value;
+    hipLaunchKernelGGL((bag_codebook_kernel<IdxT, NP, 4>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                       st, packed, S, total_rows, table_offsets, T, B, dim, indices, offsets, nnz,
+                       w, out, err_count, n_bags);
+    return launched();
+  };
+  auto by_np = [&](auto idx_tag) {
+    switch (np) {
+      case 1: return go(idx_tag, std::integral_constant<int, 1>{});
+      case 2: return go(idx_tag, std::integral_constant<int, 2>{});
+      case 3:
+      case 4: return go(idx_tag, std::integral_constant<int, 4>{});
+      default: return go(idx_tag, std::integral_constant<int, 8>{});
+    }
+  };
+  return index_type == QEMB_INDEX_INT64 ? by_np(int64_t{}) : by_np(int32_t{});
+}
+
+int qemb_l2_error_codebook(const float* x, const uint8_t* packed, int64_t rows, int32_t dim,
+                           void* workspace, double* out4, qemb_stream_t stream) {
+  if (rows < 0 || dim < 1) return QEMB_E_INVALID_ARG;
+  if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
+  if (!workspace || !out4 || (rows > 0 && (!x || !packed))) return QEMB_E_INVALID_ARG;
+  if ((x && !aligned16(x)) || (packed && !aligned16(packed)) || !aligned16(workspace))
+    return QEMB_E_MISALIGNED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  double* part = reinterpret_cast<double*>(workspace);
+  hipLaunchKernelGGL(l2_partial_codebook_kernel, dim3(kL2Blocks), dim3(kBlock), 0, st, x, packed,
+                     rows, dim, (int)qemb_codebook_row_stride(dim), part);
+  if (launched() != QEMB_OK) return QEMB_E_LAUNCH;
+  hipLaunchKernelGGL(l2_final_kernel, dim3(1), dim3(kBlock), 0, st, part, out4);
+  return launched();
+}
 
 int qemb_l2_error(const float* x, const uint8_t* packed, int64_t rows, int32_t dim, int32_t bits,
                   void* workspace, double* out4, qemb_stream_t stream) {

@@ -25,7 +25,11 @@ MAX_DIM = 1024
 EXPORTED = (
     "qemb_abi_version", "qemb_strerror", "qemb_row_stride", "qemb_quantize_rowwise",
     "qemb_dequantize", "qemb_bag_forward", "qemb_l2_error_workspace_bytes", "qemb_l2_error",
+    "qemb_codebook_row_stride", "qemb_quantize_codebook", "qemb_dequantize_codebook",
+    "qemb_bag_forward_codebook", "qemb_l2_error_codebook",
 )
+
+CODEBOOK_ITERS = 10
 
 
 class QembError(RuntimeError):
@@ -60,6 +64,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.qemb_l2_error_workspace_bytes.restype = ctypes.c_size_t
     L.qemb_l2_error.argtypes = [p, p, i64, i32, i32, p, p, p]
     L.qemb_l2_error.restype = ctypes.c_int
+    L.qemb_codebook_row_stride.argtypes = [i32]
+    L.qemb_codebook_row_stride.restype = i64
+    L.qemb_quantize_codebook.argtypes = [p, i64, i32, i32, p, p]
+    L.qemb_quantize_codebook.restype = ctypes.c_int
+    L.qemb_dequantize_codebook.argtypes = [p, i64, i32, p, p]
+    L.qemb_dequantize_codebook.restype = ctypes.c_int
+    L.qemb_bag_forward_codebook.argtypes = [p, i64, p, i32, i64, i32, p, p, i64, i32, i32, p, p, p, p]
+    L.qemb_bag_forward_codebook.restype = ctypes.c_int
+    L.qemb_l2_error_codebook.argtypes = [p, p, i64, i32, p, p, p]
+    L.qemb_l2_error_codebook.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -134,13 +148,8 @@ def dequantize(packed: torch.Tensor, dim: int, bits: int = 4,
     return out
 
 
-def bag_forward(packed: torch.Tensor, table_offsets: torch.Tensor, B: int, dim: int, bits: int,
-                indices: torch.Tensor, offsets: torch.Tensor, weights: Optional[torch.Tensor] = None,
-                pool_mode: Optional[int] = None, out: Optional[torch.Tensor] = None,
-                err_count: Optional[torch.Tensor] = None,
-                total_rows: Optional[int] = None) -> torch.Tensor:
-    """Pooled lookup: out [B, T, dim] float32; bag g = t*B + b spans
-    indices[offsets[g]:offsets[g+1]] (ids local to table t)."""
+def _bag_args(packed, table_offsets, B, dim, indices, offsets, weights, pool_mode, out,
+              err_count, total_rows):
     _dev("packed", packed, torch.uint8)
     _dev("table_offsets", table_offsets, torch.int64)
     _dev("indices", indices)
@@ -167,6 +176,19 @@ def bag_forward(packed: torch.Tensor, table_offsets: torch.Tensor, B: int, dim: 
         _dev("err_count", err_count, torch.int32)
     if total_rows is None:
         total_rows = packed.shape[0]
+    return T, itype, pool_mode, out, total_rows
+
+
+def bag_forward(packed: torch.Tensor, table_offsets: torch.Tensor, B: int, dim: int, bits: int,
+                indices: torch.Tensor, offsets: torch.Tensor, weights: Optional[torch.Tensor] = None,
+                pool_mode: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                err_count: Optional[torch.Tensor] = None,
+                total_rows: Optional[int] = None) -> torch.Tensor:
+    """Pooled lookup: out [B, T, dim] float32; bag g = t*B + b spans
+    indices[offsets[g]:offsets[g+1]] (ids local to table t)."""
+    T, itype, pool_mode, out, total_rows = _bag_args(
+        packed, table_offsets, B, dim, indices, offsets, weights, pool_mode, out, err_count,
+        total_rows)
     _check("qemb_bag_forward", load_library().qemb_bag_forward(
         _ptr(packed), total_rows, _ptr(table_offsets), T, B, dim, bits, _ptr(indices),
         _ptr(offsets), indices.numel(), itype, pool_mode, _ptr(weights), _ptr(out),
@@ -190,6 +212,83 @@ def l2_error(x: torch.Tensor, packed: torch.Tensor, bits: int,
         out4 = torch.empty(4, dtype=torch.float64, device=x.device)
     _check("qemb_l2_error", load_library().qemb_l2_error(
         _ptr(x), _ptr(packed), rows, dim, bits, _ptr(workspace), _ptr(out4), _stream(x)))
+    return _l2_dict(out4)
+
+
+def _l2_dict(out4: torch.Tensor) -> dict:
     v = out4.cpu().tolist()
     frob = (v[2] / v[3]) ** 0.5 if v[3] > 0 else 0.0
     return {"mean_row": v[0], "rows": int(v[1]), "sum_err2": v[2], "sum_x2": v[3], "frobenius": frob}
+
+
+# ---- codebook rows (16 fp32 levels per row, 4-bit codes) ----
+
+def codebook_row_stride(dim: int) -> int:
+    s = int(load_library().qemb_codebook_row_stride(dim))
+    if s < 0:
+        raise ValueError("unsupported dim=%d" % dim)
+    return s
+
+
+def quantize_codebook(x: torch.Tensor, n_iter: int = CODEBOOK_ITERS,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x [rows, dim] float32 (device) -> codebook rows [rows, stride] uint8."""
+    _dev("x", x, torch.float32)
+    rows, dim = x.shape
+    S = codebook_row_stride(dim)
+    if out is None:
+        out = torch.empty((rows, S), dtype=torch.uint8, device=x.device)
+    _dev("out", out, torch.uint8)
+    if tuple(out.shape) != (rows, S):
+        raise ValueError("out must be [%d, %d]" % (rows, S))
+    _check("qemb_quantize_codebook", load_library().qemb_quantize_codebook(
+        _ptr(x), rows, dim, n_iter, _ptr(out), _stream(x)))
+    return out
+
+
+def dequantize_codebook(packed: torch.Tensor, dim: int,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """codebook rows [rows, stride] uint8 (device) -> [rows, dim] float32."""
+    _dev("packed", packed, torch.uint8)
+    rows = packed.shape[0]
+    if packed.dim() != 2 or packed.shape[1] != codebook_row_stride(dim):
+        raise ValueError("packed must be [rows, %d]" % codebook_row_stride(dim))
+    if out is None:
+        out = torch.empty((rows, dim), dtype=torch.float32, device=packed.device)
+    _dev("out", out, torch.float32)
+    _check("qemb_dequantize_codebook", load_library().qemb_dequantize_codebook(
+        _ptr(packed), rows, dim, _ptr(out), _stream(packed)))
+    return out
+
+
+def bag_forward_codebook(packed: torch.Tensor, table_offsets: torch.Tensor, B: int, dim: int,
+                         indices: torch.Tensor, offsets: torch.Tensor,
+                         weights: Optional[torch.Tensor] = None, pool_mode: Optional[int] = None,
+                         out: Optional[torch.Tensor] = None,
+                         err_count: Optional[torch.Tensor] = None,
+                         total_rows: Optional[int] = None) -> torch.Tensor:
+    """Pooled lookup over codebook rows; the same layout as bag_forward."""
+    T, itype, pool_mode, out, total_rows = _bag_args(
+        packed, table_offsets, B, dim, indices, offsets, weights, pool_mode, out, err_count,
+        total_rows)
+    _check("qemb_bag_forward_codebook", load_library().qemb_bag_forward_codebook(
+        _ptr(packed), total_rows, _ptr(table_offsets), T, B, dim, _ptr(indices), _ptr(offsets),
+        indices.numel(), itype, pool_mode, _ptr(weights), _ptr(out), _ptr(err_count),
+        _stream(packed)))
+    return out
+
+
+def l2_error_codebook(x: torch.Tensor, packed: torch.Tensor,
+                      workspace: Optional[torch.Tensor] = None,
+                      out4: Optional[torch.Tensor] = None) -> dict:
+    """Normalized l2 error of codebook rows against x (binary64, on the device)."""
+    _dev("x", x, torch.float32)
+    _dev("packed", packed, torch.uint8)
+    rows, dim = x.shape
+    if workspace is None:
+        workspace = torch.empty(l2_error_workspace_bytes(), dtype=torch.uint8, device=x.device)
+    if out4 is None:
+        out4 = torch.empty(4, dtype=torch.float64, device=x.device)
+    _check("qemb_l2_error_codebook", load_library().qemb_l2_error_codebook(
+        _ptr(x), _ptr(packed), rows, dim, _ptr(workspace), _ptr(out4), _stream(x)))
+    return _l2_dict(out4)

@@ -1,0 +1,255 @@
+"""GPU parity of the codebook rows (16 fp32 levels per row from 1-D k-means,
+4-bit codes: "Post-Training 4-bit Quantization on Embedding Tables", review
+page, "Proposed method") against the CPU oracle.
+
+Bars: packed rows (levels, codes, padding) and decoded values bit-exact;
+error counts exact; pooled outputs within
+|gpu - oracle| <= 1e-5 * sum_p |w_p * y_pj| + 1e-6 per element; the
+normalized l2 error within 1e-12 relative.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from int4_row_wise_amd import synth
+from tests.gpu_common import assert_pooled_close, dev, host, require_gpu, special_rows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def q():
+    return require_gpu()
+
+
+DIMS = [1, 2, 3, 5, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 128, 129, 255, 256, 257,
+        511, 512, 513, 1000, 1024]
+
+
+@pytest.mark.parametrize("dim", DIMS)
+def test_quantize_codebook_bit_exact(q, dim):
+    print("codebook quantize dim=%d" % dim, flush=True)
+    g = np.random.default_rng(7000 + dim)
+    rows = 1000 + 37 if dim <= 256 else 300 + 5
+    x = special_rows(g, rows, dim)
+    ref = oracle.quantize_codebook(x)
+    got = host(q.quantize_codebook(dev(x)))
+    bad = np.nonzero(np.any(got != ref, axis=1))[0]
+    assert bad.size == 0, "rows %s differ (first: kind of row %r)" % (bad[:8], x[bad[0]][:4])
+    y = host(q.dequantize_codebook(dev(ref), dim))
+    assert np.array_equal(y.view(np.uint32), oracle.dequantize_codebook(ref, dim).view(np.uint32))
+
+
+@pytest.mark.parametrize("n_iter", [0, 1, 2, 3, 25])
+@pytest.mark.parametrize("dim", [7, 16, 64, 128, 300])
+def test_quantize_codebook_iterations(q, dim, n_iter):
+    g = np.random.default_rng(7100 + dim * 31 + n_iter)
+    x = special_rows(g, 513, dim)
+    ref = oracle.quantize_codebook(x, n_iter)
+    got = host(q.quantize_codebook(dev(x), n_iter))
+    assert np.array_equal(got, ref)
+
+
+def test_quantize_codebook_misaligned_dims_and_single_row(q):
+    """dim not a multiple of 4 takes the scalar loads; one row; rows that fill
+    the grid-stride loop more than once."""
+    for dim, rows in ((6, 1), (10, 70001), (130, 1), (66, 9000)):
+        g = np.random.default_rng(7200 + dim + rows)
+        x = (g.standard_normal((rows, dim)) * 0.05).astype(np.float32)
+        assert np.array_equal(host(q.quantize_codebook(dev(x))), oracle.quantize_codebook(x)), dim
+
+
+def test_dequantize_codebook_arbitrary_rows(q):
+    """Any finite levels and any codes decode to exact copies of the levels."""
+    g = np.random.default_rng(7300)
+    for dim in (1, 3, 16, 33, 64, 128, 129, 1000, 1024):
+        rows = 2000 + 3
+        S = oracle.codebook_row_stride(dim)
+        p = np.zeros((rows, S), np.uint8)
+        lv = (g.standard_normal((rows, 16)) * g.uniform(1e-3, 1e3, size=(rows, 1))).astype(np.float32)
+        p[:, :64] = lv.view(np.uint8)
+        C = (dim + 1) // 2
+        codes = g.integers(0, 256, size=(rows, C)).astype(np.uint8)
+        if dim % 2:
+            codes[:, -1] &= 0x0F  # the pad nibble is zero
+        p[:, 64:64 + C] = codes
+        got = host(q.dequantize_codebook(dev(p), dim))
+        assert np.array_equal(got.view(np.uint32), oracle.dequantize_codebook(p, dim).view(np.uint32)), dim
+
+
+@pytest.mark.parametrize("dim", [16, 64, 100, 1000])
+def test_l2_error_codebook_matches_oracle(q, dim):
+    g = np.random.default_rng(7400 + dim)
+    x = special_rows(g, 20000 + 17 if dim <= 100 else 2000 + 3, dim)
+    packed = oracle.quantize_codebook(x)
+    ref = oracle.l2_error_codebook(x, packed)
+    got = q.l2_error_codebook(dev(x), dev(packed))
+    assert got["rows"] == ref["rows"]
+    for k in ("mean_row", "sum_err2", "sum_x2"):
+        assert abs(got[k] - ref[k]) <= 1e-12 * abs(ref[k]) + 1e-300, (k, got[k], ref[k])
+
+
+# ---------------------------------------------------------------------------
+# pooled lookup over codebook rows
+# ---------------------------------------------------------------------------
+
+def _run(q, packed, bt, dim, weights=None, total_rows=None, itype=np.int32):
+    import torch
+    idx = bt.indices.astype(itype)
+    offs = bt.offsets.astype(itype)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = q.bag_forward_codebook(dev(packed), dev(bt.table_offsets), bt.B, dim, dev(idx), dev(offs),
+                                 None if weights is None else dev(weights), err_count=err,
+                                 total_rows=total_rows)
+    ref, absd, rerr = oracle.bag_forward_codebook(packed, bt.table_offsets, bt.B, dim, idx, offs,
+                                                  weights, total_rows=total_rows)
+    return host(out), int(host(err)[0]), ref, absd, rerr
+
+
+def _ragged(g, rows, B, max_len, dim, weighted):
+    T = len(rows)
+    lengths = g.integers(0, max_len + 1, size=T * B)
+    lengths[::11] = 0
+    offsets = np.concatenate([[0], np.cumsum(lengths)])
+    idx = np.concatenate([g.integers(0, rows[gb // B], size=lengths[gb]) for gb in range(T * B)])
+    return synth.Batch(idx.astype(np.int32), offsets.astype(np.int32),
+                       g.random(idx.size).astype(np.float32) if weighted else None,
+                       np.concatenate([[0], np.cumsum(rows)]).astype(np.int64), B, T), lengths
+
+
+@pytest.mark.parametrize("dim", [1, 3, 16, 33, 64, 100, 128, 130, 256, 300, 513, 1000, 1024])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_bag_codebook_dims_ragged_bags(q, dim, weighted):
+    print("codebook bag dim=%d weighted=%d" % (dim, weighted), flush=True)
+    g = np.random.default_rng(7500 + dim * 3 + weighted)
+    rows = [1, 57, 300]
+    x = special_rows(g, sum(rows), dim)
+    x[np.abs(x) > 100] = 1.0  # keep the tolerance meaningful
+    packed = oracle.quantize_codebook(x)
+    bt, lengths = _ragged(g, rows, 97, 70, dim, weighted)
+    got, err, ref, absd, rerr = _run(q, packed, bt, dim, bt.weights)
+    assert err == rerr == 0
+    assert_pooled_close(got, ref, absd, "codebook dim %d" % dim)
+    empty = (lengths == 0).reshape(len(rows), 97).T
+    assert np.all(got[empty] == 0) and not np.any(np.signbit(got[empty]))
+
+
+@pytest.mark.parametrize("itype", [np.int32, np.int64])
+def test_bag_codebook_multi_hot_scaled(q, itype):
+    """The multi-hot workload's shape (64 tables, d=128, bags of 1..64 ids,
+    Zipf ids, U(0,1) weights) with 3000 rows per table and batch 300."""
+    w = synth.scaled(synth.workload(4), rows=(3000,) * 64, batch=300)
+    x = np.concatenate([synth.table_values_np(w, t, 0, w.rows[t]) for t in range(w.n_tables)])
+    packed = oracle.quantize_codebook(x)
+    bt = synth.batch(w, index_dtype=np.int64)
+    got, err, ref, absd, rerr = _run(q, packed, bt, w.dim, bt.weights, itype=itype)
+    assert err == rerr == 0
+    assert_pooled_close(got, ref, absd, "codebook multi-hot")
+
+
+def test_bag_codebook_long_bags(q):
+    g = np.random.default_rng(7600)
+    dim, rows, B = 64, [700, 900], 12
+    x = special_rows(g, sum(rows), dim)
+    x[np.abs(x) > 100] = 1.0
+    packed = oracle.quantize_codebook(x)
+    lengths = np.array([0, 1, 500, 64, 65, 33, 31, 32, 1000, 2, 63, 0] * 2)
+    offsets = np.concatenate([[0], np.cumsum(lengths)])
+    idx = np.concatenate([g.integers(0, rows[gb // B], size=lengths[gb]) for gb in range(2 * B)])
+    bt = synth.Batch(idx.astype(np.int32), offsets.astype(np.int32),
+                     g.random(idx.size).astype(np.float32),
+                     np.concatenate([[0], np.cumsum(rows)]).astype(np.int64), B, 2)
+    got, err, ref, absd, rerr = _run(q, packed, bt, dim, bt.weights)
+    assert err == rerr == 0
+    assert_pooled_close(got, ref, absd, "codebook long bags")
+
+
+def test_bag_codebook_invalid_ids_offsets_and_tables(q):
+    g = np.random.default_rng(7700)
+    dim, T, B = 64, 4, 50
+    rows = [100, 10, 1, 40]
+    x = special_rows(g, sum(rows), dim)
+    x[np.abs(x) > 100] = 1.0
+    packed = oracle.quantize_codebook(x)
+    lengths = g.integers(0, 12, size=T * B)
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    idx = np.concatenate([g.integers(-5, rows[gb // B] + 5, size=lengths[gb])
+                          for gb in range(T * B)]).astype(np.int64)
+    offsets[17] = offsets[16] - 1             # decreasing
+    offsets[90] = offsets[-1] + 3             # past nnz
+    toff = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    bt = synth.Batch(idx, offsets, g.random(idx.size).astype(np.float32), toff, B, T)
+    for itype in (np.int32, np.int64):
+        got, err, ref, absd, rerr = _run(q, packed, bt, dim, bt.weights, itype=itype)
+        assert err == rerr and err > 20
+        assert_pooled_close(got, ref, absd, "codebook invalid")
+    got, err, ref, absd, rerr = _run(q, packed, bt, dim, bt.weights, total_rows=sum(rows) - 1)
+    assert err == rerr
+    assert_pooled_close(got, ref, absd, "codebook table out of range")
+    assert np.all(got[:, 3, :] == 0)
+    # an empty table: every id of it is skipped and counted
+    toff2 = np.array([0, 100, 100, 101, 151], np.int64)
+    bt2 = synth.Batch(idx, offsets, bt.weights, toff2, B, T)
+    got, err, ref, absd, rerr = _run(q, packed, bt2, dim, bt.weights)
+    assert err == rerr
+    assert_pooled_close(got, ref, absd, "codebook empty table")
+
+
+def test_bag_codebook_no_rows_no_ids_single_bag(q):
+    import torch
+    g = np.random.default_rng(7800)
+    dim = 128
+    x = special_rows(g, 20, dim)
+    packed = oracle.quantize_codebook(x)
+    toff = np.array([0, 20], np.int64)
+    bt = synth.Batch(np.zeros(0, np.int32), np.zeros(9, np.int32), None, toff, 8, 1)
+    got, err, ref, absd, rerr = _run(q, packed, bt, dim)
+    assert err == 0 and np.all(got == 0)
+    bt = synth.Batch(np.arange(20, dtype=np.int32), np.array([0, 20], np.int32), None, toff, 1, 1)
+    got, err, ref, absd, rerr = _run(q, packed, bt, dim)
+    assert err == 0
+    assert_pooled_close(got, ref, absd, "codebook single bag")
+    # no packed rows at all: every id is counted, outputs are zero
+    err_t = torch.zeros(1, dtype=torch.int32, device="cuda")
+    empty = torch.zeros((0, oracle.codebook_row_stride(dim)), dtype=torch.uint8, device="cuda")
+    out = q.bag_forward_codebook(empty, dev(np.array([0, 0], np.int64)), 1, dim,
+                                 dev(np.array([0, 3, 5], np.int32)),
+                                 dev(np.array([0, 3], np.int32)), err_count=err_t)
+    assert int(host(err_t)[0]) == 3 and np.all(host(out) == 0)
+
+
+def test_bag_codebook_weight_doubling_and_determinism(q):
+    import torch
+    w = synth.scaled(synth.workload(4), rows=(2000,) * 64, batch=128)
+    x = np.concatenate([synth.table_values_np(w, t, 0, w.rows[t]) for t in range(w.n_tables)])
+    packed = dev(oracle.quantize_codebook(x))
+    bt = synth.batch(w)
+    args = (packed, dev(bt.table_offsets), bt.B, w.dim, dev(bt.indices), dev(bt.offsets))
+    o1 = host(q.bag_forward_codebook(*args, weights=dev(bt.weights)))
+    o2 = host(q.bag_forward_codebook(*args, weights=dev(bt.weights)))
+    o3 = host(q.bag_forward_codebook(*args, weights=dev(bt.weights * np.float32(2.0))))
+    torch.cuda.synchronize()
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal((2 * o1).view(np.uint32), o3.view(np.uint32))
+
+
+def test_codebook_end_to_end_gpu_table(q):
+    """GPU quantizer -> GPU lookup, against the oracle's quantizer -> oracle
+    lookup; and the codebook's l2 loss below the range quantizer's."""
+    w = synth.scaled(synth.workload(4), rows=(1500,) * 64, batch=100)
+    x = np.concatenate([synth.table_values_np(w, t, 0, w.rows[t]) for t in range(w.n_tables)])
+    packed_ref = oracle.quantize_codebook(x)
+    xd = dev(x)
+    packed = q.quantize_codebook(xd)
+    assert np.array_equal(host(packed), packed_ref)
+    bt = synth.batch(w)
+    got = host(q.bag_forward_codebook(packed, dev(bt.table_offsets), bt.B, w.dim, dev(bt.indices),
+                                      dev(bt.offsets), dev(bt.weights)))
+    ref, absd, _ = oracle.bag_forward_codebook(packed_ref, bt.table_offsets, bt.B, w.dim,
+                                               bt.indices, bt.offsets, bt.weights)
+    assert_pooled_close(got, ref, absd, "codebook end to end")
+    cb = q.l2_error_codebook(xd, packed)["mean_row"]
+    rg = q.l2_error(xd, q.quantize_rowwise(xd, 4), 4)["mean_row"]
+    assert cb < rg
