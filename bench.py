@@ -11,8 +11,9 @@ batches rotate across steps.  The table is generated on the GPU and packed by
 the library's own quantizer before timing starts; inputs are resident in HBM.
 
 Beside it, in the same run: the INT8 table, a uniform-id control (no Zipf
-reuse), the quantizer workload (5e7 x 64 rows: range and greedy quantize,
-dequantize, normalized l2), and the CPU oracle timed on a bounded sample.
+reuse), the same lookups over k-means codebook rows, the quantizer workload
+(5e7 x 64 rows: range, greedy and codebook quantize, dequantize, normalized
+l2), and the CPU oracle timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -48,6 +49,8 @@ def parse():
     ap.add_argument("--batches", type=int, default=4, help="index batches rotated across steps")
     ap.add_argument("--no-extras", action="store_true", help="headline only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--codebook-only", action="store_true",
+                    help="only the codebook-row lookup of the multi-hot workload (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -60,6 +63,14 @@ def algorithmic_bag_bytes(nnz: int, n_bags: int, dim: int, bits: int, idx_bytes:
     offsets, and the fp32 output."""
     row = (dim * bits + 7) // 8 + 4
     per = row + idx_bytes + (4 if weighted else 0)
+    return nnz * per + (n_bags + 1) * idx_bytes + n_bags * dim * 4
+
+
+def algorithmic_codebook_bytes(nnz: int, n_bags: int, dim: int, idx_bytes: int,
+                               weighted: bool) -> int:
+    """The same minimum for codebook rows: 16 fp32 levels (64 bytes) and the
+    unpadded 4-bit codes per lookup."""
+    per = 64 + (dim + 1) // 2 + idx_bytes + (4 if weighted else 0)
     return nnz * per + (n_bags + 1) * idx_bytes + n_bags * dim * 4
 
 
@@ -138,10 +149,14 @@ def to_dev(torch, a, dev):
 
 def bench_bags(q, torch, packed, toff, batches, w, bits, steps, warmup, out):
     """Time `steps` lookups rotating over the batches; returns per-launch ms
-    (HIP events around each launch) and the wall time of the timed region."""
+    (HIP events around each launch) and the wall time of the timed region.
+    bits None: codebook rows."""
     def call(k):
         b = batches[k % len(batches)]
-        q.bag_forward(packed, toff, w.batch, w.dim, bits, b["idx"], b["offs"], b["w"], out=out)
+        if bits is None:
+            q.bag_forward_codebook(packed, toff, w.batch, w.dim, b["idx"], b["offs"], b["w"], out=out)
+        else:
+            q.bag_forward(packed, toff, w.batch, w.dim, bits, b["idx"], b["offs"], b["w"], out=out)
 
     for k in range(warmup):
         call(k)
@@ -291,9 +306,49 @@ def quantizer_extras(q, synth, torch, dev, reps=3):
                               "valu_ops_per_s": ops / ms * 1e3,
                               "valu_frac": ops / ms * 1e3 / VALU_PEAK_OPS}
     res["greedy_l2"] = q.l2_error(x, packed, 4)
-    del x, y, packed
+    del packed
+    cb = torch.empty((rows, q.codebook_row_stride(dim)), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: q.quantize_codebook(x, q.CODEBOOK_ITERS, out=cb), 1)
+    res["codebook_quantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3, "n_iter": q.CODEBOOK_ITERS,
+                                "bytes_per_row": cb.shape[1]}
+    res["codebook_l2"] = q.l2_error_codebook(x, cb)
+    cb_out = rows * cb.shape[1]
+    ms = timed(lambda: q.dequantize_codebook(cb, dim, out=y), reps)
+    res["codebook_dequantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3,
+                                  "GBps": (in_b + cb_out) / ms / 1e6,
+                                  "hbm_frac": (in_b + cb_out) / ms / 1e6 / HBM_PEAK_GBS}
+    del x, y, cb
     torch.cuda.empty_cache()
     return res
+
+
+def codebook_extras(q, synth, torch, w, toff, batches, out, dev, n_bags, steps=20, warmup=3):
+    """The multi-hot workload over codebook rows (16 fp32 levels per row from
+    k-means, 4-bit codes): the tables quantized by the library's codebook
+    quantizer, then the same rotating batches through the codebook lookup."""
+    S = q.codebook_row_stride(w.dim)
+    cb = torch.empty((w.total_rows, S), dtype=torch.uint8, device=dev)
+    tm = Timer(torch)
+    r0 = 0
+    for t in range(w.n_tables):
+        n = w.rows[t]
+        x = synth.table_values_torch(w, t, 0, n, dev)
+        with tm:
+            q.quantize_codebook(x, q.CODEBOOK_ITERS, out=cb[r0:r0 + n])
+        del x
+        r0 += n
+    qms = float(np.sum(tm.ms()))
+    ms, _ = bench_bags(q, torch, cb, toff, batches, w, None, steps, warmup, out)
+    nnz = [batches[k % len(batches)]["nnz"] for k in range(steps)]
+    byt = [algorithmic_codebook_bytes(n, n_bags, w.dim, 4, True) for n in nnz]
+    gbps = float(np.mean(byt)) / (np.mean(ms) * 1e-3) / 1e9
+    del cb
+    torch.cuda.empty_cache()
+    return {"quantize_ms_all_tables": qms, "quantize_rows_per_s": w.total_rows / qms * 1e3,
+            "n_iter": q.CODEBOOK_ITERS, "row_bytes": S,
+            "lookups_per_s": float(np.mean(nnz)) / (np.mean(ms) * 1e-3),
+            "avg_launch_ms": float(np.mean(ms)), "launch_ms": launch_stats(ms),
+            "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBS}
 
 
 def main():
@@ -326,7 +381,7 @@ def main():
     bits_list = (4,) if args.no_extras else (4, 8)
 
     t0 = time.time()
-    packed = build_table(q, synth, torch, w, bits_list, dev)
+    packed = {} if args.codebook_only else build_table(q, synth, torch, w, bits_list, dev)
     log("tables generated and packed in %.1fs" % (time.time() - t0))
     toff = to_dev(torch, np.array([0] + list(np.cumsum(w.rows)), dtype=np.int64), dev)
     t0 = time.time()
@@ -340,6 +395,12 @@ def main():
         len(batches), time.time() - t0, [b["nnz"] for b in batches]))
     n_bags = w.n_tables * w.batch
     out = torch.empty((w.batch, w.n_tables, w.dim), dtype=torch.float32, device=dev)
+    if args.codebook_only:
+        del packed
+        res = codebook_extras(q, synth, torch, w, toff, batches, out, dev, n_bags, args.steps,
+                              args.warmup)
+        print(json.dumps({"codebook": res, "workload": w.name}), flush=True)
+        return
 
     ms, wall = bench_bags(q, torch, packed[4], toff, batches, w, 4, args.steps, args.warmup, out)
     nnz_timed = sum(batches[k % len(batches)]["nnz"] for k in range(args.steps))
@@ -413,6 +474,7 @@ def main():
         result["device_copy_GBps"] = device_copy_gbps(torch, dev)
         del packed[8]
         torch.cuda.empty_cache()
+        result["codebook"] = codebook_extras(q, synth, torch, w, toff, batches, out, dev, n_bags)
         t0 = time.time()
         result["quantizer"] = quantizer_extras(q, synth, torch, dev)
         log("quantizer workload done in %.1fs" % (time.time() - t0))

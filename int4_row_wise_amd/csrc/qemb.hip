@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(kBlock) void bag_stream_kernel(
     } else {
       ok = in && (uint32_t)idr < (uint64_t)tab_nt;
     }
-    errs += __builtin_popcountll(__ballot(in && !ok));
+    errs += (in && !ok) ? 1 : 0;  // the id's owner lane counts it
     R.w = ok ? wl : 0.0f;
     if constexpr (decltype(BUF_)::value) {
       const uint32_t own = ok ? (uint32_t)idr * (uint32_t)S : kBufOut;
@@ -1577,9 +1577,19 @@ __global__ __launch_bounds__(kBlock) void dequant_codebook_kernel(
 }
 
 // Pooled lookup over codebook rows: one wave per bag, 4 row groups of 16
-// lanes (lane k of a group holds level k of the group's current row and the
-// codes of 8 elements per 128-element pass); U rows per group in flight.
-// The groups' partial sums are added by xor shuffles across 16 and 32.
+// lanes; lane k of a group holds level k of the group's current row and the
+// code word of elements [8k, 8k+8) of every 128-element pass.  The bag's ids
+// are read 64 at a time, one per owner lane, which checks it; row offsets and
+// weights reach the groups by ds_bpermute, so 4*U rows are in flight after
+// one wait for the ids.  Tables below kBufLimit bytes are read through a
+// buffer descriptor with 32-bit offsets (an absent row reads zeros), larger
+// ones with 64-bit addresses.
+//
+// Decoding an element is one ds_bpermute from the lane that holds its level:
+// ds_bpermute selects the source lane by address bits [7:2] and ignores the
+// bits above, so a byte holding (group lane base + code) * 4 is an address
+// as it stands; a code word gives two words of four such bytes each (even
+// and odd elements), and a shift moves each byte to the bottom.
 template <typename IdxT, int NP, int U>
 __global__ __launch_bounds__(kBlock) void bag_codebook_kernel(
     const uint8_t* __restrict__ packed, int64_t S, int64_t total_rows,
@@ -1587,19 +1597,21 @@ __global__ __launch_bounds__(kBlock) void bag_codebook_kernel(
     const void* __restrict__ indices, const void* __restrict__ offsets, int64_t nnz,
     const float* __restrict__ weights, float* __restrict__ out, int32_t* __restrict__ err_count,
     int64_t n_bags) {
+  static_assert(16 % U == 0, "U divides the 16 rounds of a 64-id chunk");
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
-  const int k = lane % kCbLevels, gbase = lane - k, grp = lane / kCbLevels;
-  const int64_t bag = ((int64_t)blockIdx.x * kBlock + threadIdx.x) / kWave;
-  if (bag >= n_bags) return;
+  const int k = lane % kCbLevels, grp = lane / kCbLevels;
+  const int64_t bag = (int64_t)blockIdx.x * kWPB + wv;
+  if (bag >= n_bags) return;  // whole waves leave together
   const int64_t t = bag / B, b = bag - t * B;
   int errs = 0;
   int64_t p0 = load_index<IdxT>(offsets, bag), p1 = load_index<IdxT>(offsets, bag + 1);
-  if (!(p0 >= 0 && p1 >= p0 && p1 <= nnz)) {
+  if (!uniform_flag(p0 >= 0 && p1 >= p0 && p1 <= nnz)) {
     errs = lane == 0 ? 1 : 0;
     p0 = p1 = 0;
   }
   const int64_t a0 = table_offsets[t], a1 = table_offsets[t + 1];
-  const bool tab_ok = a0 >= 0 && a1 > a0 && a1 <= total_rows;
+  const bool tab_ok = uniform_flag(a0 >= 0 && a1 > a0 && a1 <= total_rows);
   const int64_t nt = tab_ok ? a1 - a0 : 0;
   const uint8_t* base = packed + (tab_ok ? a0 : 0) * S;
   const IdxT* ids = reinterpret_cast<const IdxT*>(indices);
@@ -1608,50 +1620,100 @@ __global__ __launch_bounds__(kBlock) void bag_codebook_kernel(
     errs += lane == 0 ? (int)(p1 - p0) : 0;
     p1 = p0;
   }
+  const int64_t tab_bytes = nt * S;
+  const bool use_buf = uniform_flag(tab_bytes < (int64_t)kBufLimit);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)base, (short)0, use_buf ? (int)tab_bytes : 0, kBufWord3);
+  const uint32_t gsel = (uint32_t)(grp * 64) * 0x01010101u;  // group lane base * 4, every byte
+  const uint32_t kmask = 0x3C3C3C3Cu;
   float acc[NP][8];
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[pp][j] = 0.0f;
-  for (int64_t q = p0; q < p1; q += 4 * U) {
-    float lv[U], wl[U];
-    uint32_t cwd[U][NP];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t pos = q + u * 4 + grp;
-      const bool in = pos < p1;
-      const int64_t id = in ? (int64_t)ids[pos] : 0;
+
+  auto body = [&](auto BUF_) {
+    constexpr bool BUF = decltype(BUF_)::value;
+    for (int64_t c = p0; c < p1; c += kWave) {
+      const int n = (int)min<int64_t>(kWave, p1 - c);
+      const bool in = lane < n;
+      const int64_t id = in ? (int64_t)ids[c + lane] : 0;
       const bool ok = in && id >= 0 && id < nt;
-      errs += (in && !ok && k == 0) ? 1 : 0;
-      const uint8_t* prow = base + (ok ? id : 0) * S;
-      wl[u] = ok ? (weights ? weights[pos] : 1.0f) : 0.0f;
-      lv[u] = *reinterpret_cast<const float*>(prow + 4 * k);
-#pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
-        const int e0 = pp * 128 + 8 * k;
-        cwd[u][pp] = e0 < dim ? *reinterpret_cast<const uint32_t*>(prow + 64 + e0 / 2) : 0u;
+      errs += (in && !ok) ? 1 : 0;
+      const int wt = __builtin_bit_cast(int, ok ? (weights ? weights[c + lane] : 1.0f) : 0.0f);
+      uint32_t own_lo, own_hi = 0;
+      if constexpr (BUF) {
+        own_lo = ok ? (uint32_t)id * (uint32_t)S : kBufOut;
+      } else {
+        const int64_t off = (ok ? id : 0) * S;  // absent: row 0, weight 0
+        own_lo = (uint32_t)off;
+        own_hi = (uint32_t)(off >> 32);
       }
-    }
+      const int nr = (n + 3) / 4;  // rounds of 4 rows, one per group
+      for (int r0 = 0; r0 < nr; r0 += U) {
+        float lv[U], wl[U];
+        uint32_t cwd[U][NP];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < U; ++u) {
+          if (r0 + u < nr) {
+            const int src = 16 * (r0 + u) + 4 * grp;  // owner lane 4(r0+u) + grp
+            wl[u] = __builtin_bit_cast(float, (int)bperm(src, (uint32_t)wt));
+            const uint32_t o = bperm(src, own_lo);
+            if constexpr (BUF) {
+              const uint32_t vo = o + 4 * k;
+              lv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, vo, 0, 0));
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp) {
+              for (int pp = 0; pp < NP; ++pp)
+                cwd[u][pp] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, vo + 64 + 64 * pp, 0, 0);
+            } else {
+              const uint64_t hi = bperm(src, own_hi);
+              const uint8_t* prow = base + ((hi << 32) | o);
+              lv[u] = *reinterpret_cast<const float*>(prow + 4 * k);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float yv = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                                          (gbase + (int)((cwd[u][pp] >> (4 * j)) & 15u)) * 4,
-                                                          __builtin_bit_cast(int, lv[u])));
-          acc[pp][j] = __builtin_fmaf(wl[u], yv, acc[pp][j]);
+              for (int pp = 0; pp < NP; ++pp) {
+                const int e0 = pp * 128 + 8 * k;
+                cwd[u][pp] = e0 < dim ? *reinterpret_cast<const uint32_t*>(prow + 64 + e0 / 2) : 0u;
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (r0 + u < nr) {
+            const uint32_t lvb = __builtin_bit_cast(uint32_t, lv[u]);
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp) {
+              const uint32_t ev = ((cwd[u][pp] << 2) & kmask) | gsel;  // elements 0,2,4,6
+              const uint32_t od = ((cwd[u][pp] >> 2) & kmask) | gsel;  // elements 1,3,5,7
+#pragma unroll
+              for (int h = 0; h < 4; ++h) {
+                const float y0 = __builtin_bit_cast(float, bperm((int)(ev >> (8 * h)), lvb));
+                const float y1 = __builtin_bit_cast(float, bperm((int)(od >> (8 * h)), lvb));
+                acc[pp][2 * h] = __builtin_fmaf(wl[u], y0, acc[pp][2 * h]);
+                acc[pp][2 * h + 1] = __builtin_fmaf(wl[u], y1, acc[pp][2 * h + 1]);
+              }
+            }
+          }
         }
       }
     }
+  };
+  if (use_buf) {
+    body(std::true_type{});
+  } else {
+    body(std::false_type{});
   }
+  // the 4 groups' partial sums: lanes i, i^32, i^16, i^48
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      acc[pp][j] += __shfl_xor(acc[pp][j], 16);
-      acc[pp][j] += __shfl_xor(acc[pp][j], 32);
+      float x0 = acc[pp][j], x1 = acc[pp][j];
+      permlane32_swap(x0, x1);
+      const float h = x0 + x1;
+      float y0 = h, y1 = h;
+      permlane16_swap(y0, y1);
+      acc[pp][j] = y0 + y1;
     }
   if (grp == 0) {
     float* o = out + (b * T + t) * (int64_t)dim;
@@ -2145,7 +2207,8 @@ int qemb_bag_forward_codebook(const uint8_t* packed, int64_t total_rows,
   auto go = [&](auto idx_tag, auto np_tag) {
     using IdxT = decltype(idx_tag);
     constexpr int NP = decltype(np_tag)::value;
-    hipLaunchKernelGGL((bag_codebook_kernel<IdxT, NP, 4>), dim3((unsigned)blocks), dim3(kBlock), 0,
+    constexpr int U = NP == 1 ? 8 : NP == 2 ? 4 : NP == 4 ? 4 : 2;
+    hipLaunchKernelGGL((bag_codebook_kernel<IdxT, NP, U>), dim3((unsigned)blocks), dim3(kBlock), 0,
                        st, packed, S, total_rows, table_offsets, T, B, dim, indices, offsets, nnz,
                        w, out, err_count, n_bags);
     return launched();

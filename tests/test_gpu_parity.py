@@ -262,6 +262,39 @@ def test_bag_invalid_ids_and_offsets_are_skipped_and_counted(q):
     assert np.all(got[:, 3, :] == 0)
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("dim", [16, 32, 64, 128, 256, 512, 1000])
+def test_bag_invalid_ids_in_long_bags(q, dim, bits):
+    """Invalid ids, bad offsets and a table out of range in multi-hot bags
+    (mean length well above 8: the one-wave-per-run lookups), each counted
+    exactly once."""
+    print("invalid ids, long bags dim=%d bits=%d" % (dim, bits), flush=True)
+    g = np.random.default_rng(6200 + dim + bits)
+    T, B = 3, 70
+    rows = [300, 20, 150]
+    x = special_rows(g, sum(rows), dim)
+    x[np.abs(x) > 100] = 1.0
+    packed = oracle.quantize_rowwise(x, bits)
+    lengths = g.integers(8, 90, size=T * B)
+    lengths[::13] = 0
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    idx = np.concatenate([g.integers(-3, rows[gb // B] + 3, size=lengths[gb])
+                          for gb in range(T * B)]).astype(np.int64)
+    offsets[40] = offsets[39] - 1             # decreasing
+    offsets[150] = offsets[-1] + 7            # past nnz
+    toff = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    bt = synth.Batch(idx, offsets, g.random(idx.size).astype(np.float32), toff, B, T)
+    for itype in (np.int32, np.int64):
+        got, err, ref, absd, rerr = _run_bag(q, packed, bt, dim, bits, bt.weights, itype=itype)
+        assert err == rerr and err > 50, (err, rerr)
+        assert_pooled_close(got, ref, absd, "invalid ids, long bags")
+    got, err, ref, absd, rerr = _run_bag(q, packed, bt, dim, bits, bt.weights,
+                                         total_rows=sum(rows) - 1)
+    assert err == rerr, (err, rerr)
+    assert_pooled_close(got, ref, absd, "long bags, table out of range")
+    assert np.all(got[:, 2, :] == 0)
+
+
 def test_bag_no_ids_and_single_bag(q):
     g = np.random.default_rng(6100)
     dim, bits = 128, 4
