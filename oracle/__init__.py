@@ -92,6 +92,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_bag_forward_codebook.restype = i32
         L.oracle_l2_error_codebook.argtypes = [p, p, i64, i32, p]
         L.oracle_l2_error_codebook.restype = i32
+        L.oracle_interaction_width.argtypes = [i32, i32]
+        L.oracle_interaction_width.restype = i64
+        L.oracle_dot_interaction.argtypes = [p, p, i64, i32, i32, p, p]
+        L.oracle_dot_interaction.restype = i32
         _lib = L
     return _lib
 
@@ -298,3 +302,26 @@ def l2_error_codebook(x: np.ndarray, packed: np.ndarray) -> dict:
     frob = float(np.sqrt(out[2] / out[3])) if out[3] > 0 else 0.0
     return {"mean_row": float(out[0]), "rows": int(out[1]), "sum_err2": float(out[2]),
             "sum_x2": float(out[3]), "frobenius": frob}
+
+
+def interaction_width(T: int, dim: int) -> int:
+    return int(lib().oracle_interaction_width(T, dim))
+
+
+def dot_interaction(dense: np.ndarray, pooled: np.ndarray):
+    """dense [B, d] float32, pooled [B, T, d] float32 -> (out [B, d + T(T+1)/2]
+    float64, abs_terms of the same shape): the dense vector, then the dot
+    products of every pair of distinct rows of Z = [dense; pooled], row by
+    row (pairs (1,0), (2,0), (2,1), (3,0), ...)."""
+    dense = np.ascontiguousarray(dense, dtype=np.float32)
+    pooled = np.ascontiguousarray(pooled, dtype=np.float32)
+    B, T, dim = pooled.shape
+    if dense.shape != (B, dim):
+        raise ValueError("dense must be [B, d]")
+    W = interaction_width(T, dim)
+    out = np.empty((B, W), dtype=np.float64)
+    absd = np.empty((B, W), dtype=np.float64)
+    rc = lib().oracle_dot_interaction(_ptr(dense), _ptr(pooled), B, T, dim, _ptr(out), _ptr(absd))
+    if rc != 0:
+        raise OracleError("oracle_dot_interaction returned %d" % rc)
+    return out, absd

@@ -28,6 +28,13 @@
  *    18.8%-37.5% of the fp32 size, i.e. 4-bit codes plus 16 fp32 levels per
  *    row at d = 256 and d = 64).  The clustering is 1-D Lloyd iteration from
  *    the row's uniform grid, a fixed number of times (rules below).
+ *  - Dot interaction of the pooled embeddings ("Deep Learning Recommendation
+ *    Model ..." review page, "Proposed method": explicit second-order
+ *    interactions are dot products between the embedding vectors and the
+ *    processed dense features, concatenated with those dense features).
+ *    Per sample the dense vector and the T pooled vectors are the rows of a
+ *    (T+1) x d matrix Z; the output is the dense vector followed by
+ *    <z_i, z_j> for every pair 0 <= j < i <= T, row by row.
  *
  * The pages give no formulas.  The numeric rules used here (binary32 RNE with
  * one rounding per written operation, no contraction, IEEE division, fp16
@@ -667,4 +674,54 @@ int oracle_l2_error(const float* x, const uint8_t* packed, int64_t rows, int dim
 int oracle_l2_error_codebook(const float* x, const uint8_t* packed, int64_t rows, int dim,
                              double* out4) {
   return l2_error_fmt(x, packed, rows, dim, OR_FMT_CB, out4);
+}
+
+/* ------------------------------------------------------------------ */
+/* Dot interaction of pooled embeddings.                                */
+/* ------------------------------------------------------------------ */
+
+/* Output width of one sample: d dense values + T(T+1)/2 dots. */
+int64_t oracle_interaction_width(int T, int dim) {
+  if (T < 0 || dim < 1) return -1;
+  return (int64_t)dim + (int64_t)T * (T + 1) / 2;
+}
+
+/* Per sample b: Z row 0 = dense[b], Z row 1 + t = pooled[b][t] (the lookup's
+   [B][T][d] output).  out[b] = dense[b] (copied) followed by, for i = 1..T
+   and j = 0..i-1 in that order, sum_k Z[i][k] * Z[j][k] in binary64 (each
+   product of two fp32 values is exact in binary64; the sum runs over k in
+   order).  abs_terms[b] (nullable) holds sum_k |Z[i][k] * Z[j][k]| at the
+   same positions and 0 at the dense positions. */
+int oracle_dot_interaction(const float* dense, const float* pooled, int64_t B, int T, int dim,
+                           double* out, double* abs_terms) {
+  if (B < 0 || T < 0 || dim < 1) return OR_INVALID;
+  const int64_t W = oracle_interaction_width(T, dim);
+#pragma omp parallel for schedule(static)
+  for (int64_t b = 0; b < B; ++b) {
+    double* o = out + b * W;
+    double* a = abs_terms ? abs_terms + b * W : NULL;
+    const float* x = dense + b * (int64_t)dim;
+    const float* e = pooled + b * (int64_t)T * dim;
+    for (int k = 0; k < dim; ++k) {
+      o[k] = (double)x[k];
+      if (a) a[k] = 0.0;
+    }
+    int64_t pos = dim;
+    for (int i = 1; i <= T; ++i) {
+      const float* zi = e + (int64_t)(i - 1) * dim;
+      for (int j = 0; j < i; ++j) {
+        const float* zj = j == 0 ? x : e + (int64_t)(j - 1) * dim;
+        double s = 0.0, sa = 0.0;
+        for (int k = 0; k < dim; ++k) {
+          double p = (double)zi[k] * (double)zj[k];
+          s += p;
+          sa += fabs(p);
+        }
+        o[pos] = s;
+        if (a) a[pos] = sa;
+        ++pos;
+      }
+    }
+  }
+  return OR_OK;
 }
