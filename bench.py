@@ -11,7 +11,8 @@ batches rotate across steps.  The table is generated on the GPU and packed by
 the library's own quantizer before timing starts; inputs are resident in HBM.
 
 Beside it, in the same run: the INT8 table, a uniform-id control (no Zipf
-reuse), the same lookups over k-means codebook rows, the quantizer workload
+reuse), the same lookups over k-means codebook rows, the dot interaction
+of the pooled output with a dense vector per sample, the quantizer workload
 (5e7 x 64 rows: range, greedy and codebook quantize, dequantize, normalized
 l2), and the CPU oracle timed on a bounded sample.
 
@@ -31,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
 VALU_PEAK_OPS = 256 * 64 * 2.4e9  # lane-ops/s: 256 CUs x 64 lanes x 2.4 GHz (no packed fp32)
 HEADLINE_KERNEL = "bag_stream_kernel<4, 8, int, true, true, true>"
 KERNEL_SOURCE = os.path.join(ROOT, "int4_row_wise_amd", "csrc", "qemb.hip")
@@ -51,6 +53,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--codebook-only", action="store_true",
                     help="only the codebook-row lookup of the multi-hot workload (for profiling)")
+    ap.add_argument("--interaction-only", action="store_true",
+                    help="only one INT4 lookup and the dot interaction on its output (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -351,6 +355,41 @@ def codebook_extras(q, synth, torch, w, toff, batches, out, dev, n_bags, steps=2
             "GBps": gbps, "hbm_frac": gbps / HBM_PEAK_GBS}
 
 
+def interaction_extras(q, torch, pooled, w, dev, steps=20, warmup=3):
+    """The dot interaction on the lookup's pooled output of the multi-hot
+    workload (B=16384 samples, T=64 tables, d=128) with a N(0,1) dense
+    vector per sample: the dense vector, then the dots of every pair of
+    distinct rows of [dense; pooled]."""
+    B, T, dim = pooled.shape
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    dense = torch.randn((B, dim), generator=gen, device=dev, dtype=torch.float32)
+    W = q.interaction_width(T, dim)
+    res_out = torch.empty((B, W), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        q.dot_interaction(dense, pooled, out=res_out)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for _ in range(steps):
+        with tm:
+            q.dot_interaction(dense, pooled, out=res_out)
+    ms = float(np.mean(tm.ms()))
+    # bytes: every input row read once, the output row written once
+    byt = B * (4 * dim * (T + 1) + 4 * W)
+    # matrix-core flops issued: 16x16 tiles on or below the diagonal of the
+    # pooled Gram matrix, 2*16*16*16 flops per 16 columns
+    nbp = (T + 15) // 16
+    kc = (dim + 15) // 16
+    mfma_flops = B * (nbp * (nbp + 1) // 2) * kc * 2 * 16 * 16 * 16
+    useful = B * 2 * dim * T * (T + 1) // 2
+    return {"samples": B, "tables": T, "dim": dim, "out_width": W, "avg_launch_ms": ms,
+            "samples_per_s": B / (ms * 1e-3), "GBps": byt / (ms * 1e-3) / 1e9,
+            "hbm_frac": byt / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_TFLOPs": mfma_flops / (ms * 1e-3) / 1e12,
+            "mfma_frac": mfma_flops / (ms * 1e-3) / 1e12 / MFMA_F32_PEAK_TFLOPS,
+            "useful_TFLOPs": useful / (ms * 1e-3) / 1e12, "bytes_per_launch": byt}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -378,7 +417,7 @@ def main():
     q.load_library()
     dev = torch.device("cuda:0")
     w = synth.workload(4)
-    bits_list = (4,) if args.no_extras else (4, 8)
+    bits_list = (4,) if (args.no_extras or args.interaction_only) else (4, 8)
 
     t0 = time.time()
     packed = {} if args.codebook_only else build_table(q, synth, torch, w, bits_list, dev)
@@ -395,6 +434,12 @@ def main():
         len(batches), time.time() - t0, [b["nnz"] for b in batches]))
     n_bags = w.n_tables * w.batch
     out = torch.empty((w.batch, w.n_tables, w.dim), dtype=torch.float32, device=dev)
+    if args.interaction_only:
+        b0 = batches[0]
+        q.bag_forward(packed[4], toff, w.batch, w.dim, 4, b0["idx"], b0["offs"], b0["w"], out=out)
+        res = interaction_extras(q, torch, out, w, dev, args.steps, args.warmup)
+        print(json.dumps({"interaction": res, "workload": w.name}), flush=True)
+        return
     if args.codebook_only:
         del packed
         res = codebook_extras(q, synth, torch, w, toff, batches, out, dev, n_bags, args.steps,
@@ -471,6 +516,7 @@ def main():
             "note": "each launch after writing a 1 GiB scratch buffer (L2 and MALL flushed)",
             "launch_ms": launch_stats(msc), "GBps": b0 / (np.median(msc) * 1e-3) / 1e9,
             "hbm_frac": b0 / (np.median(msc) * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        result["interaction"] = interaction_extras(q, torch, out, w, dev)
         result["device_copy_GBps"] = device_copy_gbps(torch, dev)
         del packed[8]
         torch.cuda.empty_cache()

@@ -82,6 +82,7 @@ typedef struct ihipStream_t* qemb_stream_t; /* the same type as hipStream_t */
 #define QEMB_E_LAUNCH -4      /* the HIP runtime rejected a kernel launch */
 
 #define QEMB_MAX_DIM 1024
+#define QEMB_MAX_INTERACTION_T 1024 /* tables per sample in qemb_dot_interaction */
 
 #define QEMB_CLIP_RANGE 0
 #define QEMB_CLIP_GREEDY 1
@@ -231,6 +232,34 @@ int qemb_bag_forward_codebook(const uint8_t* packed, int64_t total_rows,
  */
 int qemb_l2_error_codebook(const float* x, const uint8_t* packed, int64_t rows, int32_t dim,
                            void* workspace, double* out4, qemb_stream_t stream);
+
+/*
+ * Dot interaction of the pooled embeddings ("Deep Learning Recommendation
+ * Model for Personalization and Recommendation Systems", review page,
+ * "Proposed method": explicit second-order interactions are the dot products
+ * between the embedding vectors and the processed dense features, and they
+ * are concatenated with those dense features).
+ *
+ * Per sample b, Z is the (T+1) x dim matrix whose row 0 is dense[b] and
+ * whose row 1 + t is pooled[b][t].  The output row is
+ *   out[b] = [ dense[b][0..dim) , <z_i, z_j> for i = 1..T, j = 0..i-1 ]
+ * (pairs row by row over the strict lower triangle: (1,0), (2,0), (2,1),
+ * (3,0), ...), dim + T(T+1)/2 floats; see qemb_interaction_width.
+ *   dense   [B][dim] fp32 (the bottom MLP's output), 16-byte aligned
+ *   pooled  [B][T][dim] fp32, 16-byte aligned: exactly the output layout of
+ *           qemb_bag_forward / qemb_bag_forward_codebook
+ *   out     [B][dim + T(T+1)/2] fp32, 16-byte aligned base (rows are packed
+ *           back to back, so a row is 16-byte aligned only when its width is
+ *           a multiple of 4)
+ *   B >= 0 (0 = nothing to do), 0 <= T <= QEMB_MAX_INTERACTION_T,
+ *   1 <= dim <= QEMB_MAX_DIM
+ * The dense part is copied exactly.  Each dot is accumulated in fp32 (the
+ * pooled-pooled ones on the matrix cores) in a fixed order, so results
+ * repeat exactly; the error of each is within dim * 2^-23 * sum_k |z_ik z_jk|.
+ */
+int64_t qemb_interaction_width(int32_t T, int32_t dim);
+int qemb_dot_interaction(const float* dense, const float* pooled, int64_t B, int32_t T,
+                         int32_t dim, float* out, qemb_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1767,6 +1767,316 @@ __global__ __launch_bounds__(kBlock) void l2_partial_codebook_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// dot interaction of the pooled embeddings ("Deep Learning Recommendation
+// Model ..." review page, "Proposed method": second-order interactions are
+// the dot products between the embedding vectors and the processed dense
+// features, concatenated with the dense features).  Per sample b the rows of
+// Z are the dense vector (row 0) and the T pooled vectors (rows 1..T, the
+// lookup's [B][T][d] output); out[b] = dense[b], then <z_i, z_j> for
+// i = 1..T, j = 0..i-1 in that order: the pair (t1 + 1, t2 + 1) of pooled
+// rows t2 < t1 sits at d + (t1 + 1) t1 / 2 + t2 + 1, the pair (t + 1, 0)
+// with the dense vector at d + (t + 1) t / 2.
+//
+// Pooled x pooled dots are 16 x 16 tiles of the Gram matrix on the matrix
+// cores (v_mfma_f32_16x16x4_f32, fp32 in and out): lane l supplies row l % 16
+// of each operand block at k-slot l / 16, so a lane holding the float4 of
+// columns [16s + 4g, 16s + 4g + 4) of its row feeds four MFMAs, and the
+// result tile leaves rows 4g..4g+3 of column l % 16 in the lane.  Only the
+// tiles on or below the diagonal are computed.  The dense dots are plain
+// FMAs on the vector ALU with a reduction across the four k-slots.
+// ---------------------------------------------------------------------------
+
+using f32x4 = __attribute__((ext_vector_type(4))) float;
+using u32x4 = __attribute__((ext_vector_type(4))) unsigned int;
+
+// columns [k, k+4) of a row (zeros past dim or for an absent row)
+__device__ __forceinline__ float4 ix_chunk(const float* row, int k, int dim, bool vec4) {
+  float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  if (row != nullptr) {
+    if (vec4 && k + 4 <= dim) {
+      v = *reinterpret_cast<const float4*>(row + k);
+    } else {
+      if (k < dim) v.x = row[k];
+      if (k + 1 < dim) v.y = row[k + 1];
+      if (k + 2 < dim) v.z = row[k + 2];
+      if (k + 3 < dim) v.w = row[k + 3];
+    }
+  }
+  return v;
+}
+
+__device__ __forceinline__ f32x4 mfma4(float4 a, float4 b, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
+  return c;
+}
+
+// sum over the four lanes of a column (lanes c, c+16, c+32, c+48)
+__device__ __forceinline__ float ix_col_sum(float v) {
+  float a = v, b = v;
+  permlane32_swap(a, b);
+  const float h = a + b;
+  float c = h, d = h;
+  permlane16_swap(c, d);
+  return c + d;
+}
+
+__device__ __forceinline__ void ix_store_tile(float* ob, f32x4 acc, int I, int J, int r, int g, int T,
+                                              int dim) {
+  const int t2 = 16 * J + r;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int t1 = 16 * I + 4 * g + v;
+    if (t2 < t1 && t1 < T) ob[dim + (int64_t)(t1 + 1) * t1 / 2 + t2 + 1] = acc[v];
+  }
+}
+
+// NBP blocks of 16 pooled rows (T <= 16 NBP) and KC chunks of 16 columns
+// (dim <= 16 KC), all held in registers: each row is read once.
+template <int NBP, int KC>
+__global__ __launch_bounds__(kBlock) void interaction_kernel(
+    const float* __restrict__ dense, const float* __restrict__ pooled, int64_t B, int T, int dim,
+    int vec4, float* __restrict__ out) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r = lane % 16, g = lane / 16;
+  const int64_t b = (int64_t)blockIdx.x * kWPB + wv;
+  if (b >= B) return;  // whole waves leave together
+  const int64_t W = dim + (int64_t)T * (T + 1) / 2;
+  const float* xb = dense + b * dim;
+  const float* eb = pooled + b * (int64_t)T * dim;
+  float* ob = out + b * W;
+  float4 z[NBP][KC], xv[KC];
+#pragma unroll
+  for (int I = 0; I < NBP; ++I) {
+    const int t = 16 * I + r;
+    const float* row = t < T ? eb + (int64_t)t * dim : nullptr;
+#pragma unroll
+    for (int s = 0; s < KC; ++s) z[I][s] = ix_chunk(row, 16 * s + 4 * g, dim, vec4);
+  }
+#pragma unroll
+  for (int s = 0; s < KC; ++s) xv[s] = ix_chunk(xb, 16 * s + 4 * g, dim, vec4);
+  for (int k = lane; k < dim; k += kWave) ob[k] = xb[k];
+  // dots with the dense vector
+#pragma unroll
+  for (int I = 0; I < NBP; ++I) {
+    float p = 0.0f;
+#pragma unroll
+    for (int s = 0; s < KC; ++s) {
+      p = __builtin_fmaf(z[I][s].x, xv[s].x, p);
+      p = __builtin_fmaf(z[I][s].y, xv[s].y, p);
+      p = __builtin_fmaf(z[I][s].z, xv[s].z, p);
+      p = __builtin_fmaf(z[I][s].w, xv[s].w, p);
+    }
+    p = ix_col_sum(p);
+    const int t = 16 * I + r;
+    if (g == 0 && t < T) ob[dim + (int64_t)(t + 1) * t / 2] = p;
+  }
+  // pooled x pooled: tiles on or below the diagonal
+#pragma unroll
+  for (int I = 0; I < NBP; ++I) {
+#pragma unroll
+    for (int J = 0; J <= I; ++J) {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < KC; ++s) acc = mfma4(z[I][s], z[J][s], acc);
+      ix_store_tile(ob, acc, I, J, r, g, T, dim);
+    }
+  }
+}
+
+// Persistent workgroups of 4 waves, one sample at a time.  The sample being
+// computed sits in LDS; the next two are in flight in two register sets
+// (about 43 KB of LDS per workgroup at d = 128: three workgroups per CU).
+// Every global access is unconditional and goes through a per-sample buffer
+// descriptor (an absent row or a column past dim takes an out-of-range
+// offset: loads read zeros, stores are dropped), and the results are staged
+// in an LDS output row written out with coalesced stores after a barrier, so
+// the number of memory operations between a sample's loads and their use is
+// static and the wait before each LDS fill covers exactly that sample.
+// Rows sit in LDS at a stride of 16 KC + 8 floats (measured: no padding costs
+// about 40 % in bank conflicts).  Wave w takes tiles w,
+// w+4, ... of the lower triangle and the dense dots of block rows w, w+4, ...;
+// results are bitwise those of interaction_kernel (same operation order).
+// Needs dim % 4 == 0; ST4: the output row width is a multiple of 4.
+template <int NBP, int KC, bool ST4>
+__global__ __launch_bounds__(kBlock) void interaction_lds_kernel(
+    const float* __restrict__ dense, const float* __restrict__ pooled, int64_t B, int T, int dim,
+    float* __restrict__ out) {
+  constexpr int ROWS = 16 * NBP, C4 = 4 * KC, RS = C4 + 2;  // row stride in float4
+  constexpr int SLOTS = ROWS * C4, PER = (SLOTS + kBlock - 1) / kBlock;
+  constexpr int NT = NBP * (NBP + 1) / 2;
+  constexpr int WMAX = 16 * KC + ROWS * (ROWS + 1) / 2;  // widest output row
+  constexpr int OUTW = (WMAX + 3) / 4 * 4;
+  static_assert(C4 <= kBlock, "the dense row fits one pass");
+  __shared__ float4 buf[1][(ROWS + 1) * RS];
+  __shared__ float obuf[OUTW];
+  const int tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int r = lane % 16, g = lane / 16;
+  const int W = dim + T * (T + 1) / 2;
+  const int c4n = dim / 4;
+  const int rowb = dim * 4;  // bytes per row
+  float4 va[PER], vb[PER], xa, xb;
+  auto fetch = [&](int64_t smp, float4 (&v)[PER], float4& xd) {
+    const bool live = smp < B;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(pooled + (live ? smp : 0) * T * (int64_t)dim), (short)0, live ? T * rowb : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(dense + (live ? smp : 0) * dim), (short)0, live ? rowb : 0, kBufWord3);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int f = tid + kBlock * u, row = f / C4, c4 = f % C4;
+      const uint32_t off = (f < SLOTS && c4 < c4n) ? (uint32_t)(row * rowb + 16 * c4) : kBufOut;
+      v[u] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, 0));
+    }
+    xd = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rx, tid < c4n ? (uint32_t)(16 * tid) : kBufOut, 0, 0));
+  };
+  auto put = [&](int bs, const float4 (&v)[PER], const float4& xd) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int f = tid + kBlock * u;
+      if (f < SLOTS) buf[bs][(f / C4) * RS + f % C4] = v[u];
+    }
+    if (tid < C4) buf[bs][ROWS * RS + tid] = xd;
+  };
+  auto compute = [&](int bs) {
+    const float* xs = reinterpret_cast<const float*>(&buf[bs][ROWS * RS]);
+    for (int k = tid; k < dim; k += kBlock) obuf[k] = xs[k];
+#pragma unroll
+    for (int I = 0; I < NBP; ++I) {
+      if (I % kWPB == wv) {
+        float p = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KC; ++s) {
+          const float4 zi = buf[bs][(16 * I + r) * RS + 4 * s + g];
+          const float4 xv = buf[bs][ROWS * RS + 4 * s + g];
+          p = __builtin_fmaf(zi.x, xv.x, p);
+          p = __builtin_fmaf(zi.y, xv.y, p);
+          p = __builtin_fmaf(zi.z, xv.z, p);
+          p = __builtin_fmaf(zi.w, xv.w, p);
+        }
+        p = ix_col_sum(p);
+        const int t = 16 * I + r;
+        if (g == 0 && t < T) obuf[dim + (t + 1) * t / 2] = p;
+      }
+    }
+#pragma unroll
+    for (int tau = 0; tau < NT; ++tau) {
+      if (tau % kWPB == wv) {
+        int I = 0, J = tau;
+        while (J > I) {
+          J -= I + 1;
+          ++I;
+        }
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < KC; ++s)
+          acc = mfma4(buf[bs][(16 * I + r) * RS + 4 * s + g], buf[bs][(16 * J + r) * RS + 4 * s + g], acc);
+        const int t2 = 16 * J + r;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t1 = 16 * I + 4 * g + v;
+          if (t2 < t1 && t1 < T) obuf[dim + (t1 + 1) * t1 / 2 + t2 + 1] = acc[v];
+        }
+      }
+    }
+  };
+  auto copy_out = [&](int64_t smp) {
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(out + smp * (int64_t)W), (short)0, W * 4, kBufWord3);
+    if constexpr (ST4) {
+#pragma unroll
+      for (int u = 0; u < (OUTW / 4 + kBlock - 1) / kBlock; ++u) {
+        const int q4 = tid + kBlock * u;
+        const float4 vv = q4 < OUTW / 4 ? reinterpret_cast<const float4*>(obuf)[q4]
+                                        : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, vv), ro,
+                                               4 * q4 < W ? (uint32_t)(16 * q4) : kBufOut, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < (OUTW + kBlock - 1) / kBlock; ++u) {
+        const int q1 = tid + kBlock * u;
+        const float vv = q1 < OUTW ? obuf[q1] : 0.0f;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, vv), ro,
+                                              q1 < W ? (uint32_t)(4 * q1) : kBufOut, 0, 0);
+      }
+    }
+  };
+  // the barrier after compute orders the LDS fill after every wave's reads,
+  // and the barrier after the fill orders it before the next compute
+  const int64_t G = gridDim.x;
+  int64_t smp = blockIdx.x;
+  fetch(smp, va, xa);
+  fetch(smp + G, vb, xb);
+  put(0, va, xa);
+  fetch(smp + 2 * G, va, xa);
+  __syncthreads();
+  while (true) {
+    compute(0);
+    __syncthreads();
+    copy_out(smp);
+    put(0, vb, xb);
+    fetch(smp + 3 * G, vb, xb);
+    __syncthreads();
+    smp += G;
+    if (smp >= B) break;
+    compute(0);
+    __syncthreads();
+    copy_out(smp);
+    put(0, va, xa);
+    fetch(smp + 3 * G, va, xa);
+    __syncthreads();
+    smp += G;
+    if (smp >= B) break;
+  }
+}
+
+// Any T and dim: the same tiles, operands re-read for every tile.
+__global__ __launch_bounds__(kBlock) void interaction_stream_kernel(
+    const float* __restrict__ dense, const float* __restrict__ pooled, int64_t B, int T, int dim,
+    int vec4, float* __restrict__ out) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int r = lane % 16, g = lane / 16;
+  const int64_t b = (int64_t)blockIdx.x * kWPB + wv;
+  if (b >= B) return;
+  const int64_t W = dim + (int64_t)T * (T + 1) / 2;
+  const float* xb = dense + b * dim;
+  const float* eb = pooled + b * (int64_t)T * dim;
+  float* ob = out + b * W;
+  for (int k = lane; k < dim; k += kWave) ob[k] = xb[k];
+  const int nbp = (T + 15) / 16;
+  for (int I = 0; I < nbp; ++I) {
+    const int ti = 16 * I + r;
+    const float* ri = ti < T ? eb + (int64_t)ti * dim : nullptr;
+    float p = 0.0f;
+    for (int k0 = 0; k0 < dim; k0 += 16) {
+      const float4 a = ix_chunk(ri, k0 + 4 * g, dim, vec4), x = ix_chunk(xb, k0 + 4 * g, dim, vec4);
+      p = __builtin_fmaf(a.x, x.x, p);
+      p = __builtin_fmaf(a.y, x.y, p);
+      p = __builtin_fmaf(a.z, x.z, p);
+      p = __builtin_fmaf(a.w, x.w, p);
+    }
+    p = ix_col_sum(p);
+    if (g == 0 && ti < T) ob[dim + (int64_t)(ti + 1) * ti / 2] = p;
+    for (int J = 0; J <= I; ++J) {
+      const int tj = 16 * J + r;
+      const float* rj = tj < T ? eb + (int64_t)tj * dim : nullptr;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int k0 = 0; k0 < dim; k0 += 16)
+        acc = mfma4(ix_chunk(ri, k0 + 4 * g, dim, vec4), ix_chunk(rj, k0 + 4 * g, dim, vec4), acc);
+      ix_store_tile(ob, acc, I, J, r, g, T, dim);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------
 
@@ -2041,6 +2351,38 @@ int dispatch_codebook(const float* x, int64_t rows, int dim, int S, int vec4, in
   }
 }
 
+template <int NBP, int KC>
+int launch_interaction(const float* dense, const float* pooled, int64_t B, int T, int dim, int vec4,
+                       float* out, hipStream_t st) {
+  hipLaunchKernelGGL((interaction_kernel<NBP, KC>), dim3((unsigned)((B + kWPB - 1) / kWPB)),
+                     dim3(kBlock), 0, st, dense, pooled, B, T, dim, vec4, out);
+  return launched();
+}
+
+template <int NBP, int KC>
+int launch_interaction_lds(const float* dense, const float* pooled, int64_t B, int T, int dim,
+                           float* out, hipStream_t st) {
+  // three workgroups per CU (about 43 KB of LDS each at d = 128)
+  const int64_t grid = B < 768 ? B : 768;
+  const int64_t W = dim + (int64_t)T * (T + 1) / 2;
+  if (W % 4 == 0 && ((uintptr_t)out & 15) == 0)
+    hipLaunchKernelGGL((interaction_lds_kernel<NBP, KC, true>), dim3((unsigned)grid), dim3(kBlock), 0,
+                       st, dense, pooled, B, T, dim, out);
+  else
+    hipLaunchKernelGGL((interaction_lds_kernel<NBP, KC, false>), dim3((unsigned)grid), dim3(kBlock), 0,
+                       st, dense, pooled, B, T, dim, out);
+  return launched();
+}
+
+template <int NBP>
+int interaction_by_kc(const float* dense, const float* pooled, int64_t B, int T, int dim, int vec4,
+                      float* out, hipStream_t st) {
+  const int kc = (dim + 15) / 16;
+  if (kc <= 2) return launch_interaction<NBP, 2>(dense, pooled, B, T, dim, vec4, out, st);
+  if (kc <= 4) return launch_interaction<NBP, 4>(dense, pooled, B, T, dim, vec4, out, st);
+  return launch_interaction<NBP, 8>(dense, pooled, B, T, dim, vec4, out, st);
+}
+
 extern "C" {
 
 int qemb_abi_version(void) { return QEMB_ABI_VERSION; }
@@ -2223,6 +2565,37 @@ int qemb_bag_forward_codebook(const uint8_t* packed, int64_t total_rows,
     }
   };
   return index_type == QEMB_INDEX_INT64 ? by_np(int64_t{}) : by_np(int32_t{});
+}
+
+int64_t qemb_interaction_width(int32_t T, int32_t dim) {
+  if (T < 0 || T > QEMB_MAX_INTERACTION_T || dim < 1 || dim > QEMB_MAX_DIM) return -1;
+  return (int64_t)dim + (int64_t)T * (T + 1) / 2;
+}
+
+int qemb_dot_interaction(const float* dense, const float* pooled, int64_t B, int32_t T,
+                         int32_t dim, float* out, qemb_stream_t stream) {
+  if (B < 0 || T < 0 || dim < 1) return QEMB_E_INVALID_ARG;
+  if (dim > QEMB_MAX_DIM || T > QEMB_MAX_INTERACTION_T) return QEMB_E_UNSUPPORTED;
+  if (B == 0) return QEMB_OK;
+  if (!dense || !out || (T > 0 && !pooled)) return QEMB_E_INVALID_ARG;
+  if (!aligned16(dense) || (pooled && !aligned16(pooled)) || !aligned16(out)) return QEMB_E_MISALIGNED;
+  if ((B + kWPB - 1) / kWPB > 0x7fffffff) return QEMB_E_UNSUPPORTED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int vec4 = dim % 4 == 0;
+  if (vec4 && dim > 64 && dim <= 128 && T > 48 && T <= 64)
+    return launch_interaction_lds<4, 8>(dense, pooled, B, T, dim, out, st);
+  if (dim <= 128 && T <= 64) {
+    switch ((T + 15) / 16) {
+      case 0:
+      case 1: return interaction_by_kc<1>(dense, pooled, B, T, dim, vec4, out, st);
+      case 2: return interaction_by_kc<2>(dense, pooled, B, T, dim, vec4, out, st);
+      case 3: return interaction_by_kc<3>(dense, pooled, B, T, dim, vec4, out, st);
+      default: return interaction_by_kc<4>(dense, pooled, B, T, dim, vec4, out, st);
+    }
+  }
+  hipLaunchKernelGGL(interaction_stream_kernel, dim3((unsigned)((B + kWPB - 1) / kWPB)), dim3(kBlock),
+                     0, st, dense, pooled, B, T, dim, vec4, out);
+  return launched();
 }
 
 int qemb_l2_error_codebook(const float* x, const uint8_t* packed, int64_t rows, int32_t dim,

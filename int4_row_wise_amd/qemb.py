@@ -26,7 +26,8 @@ EXPORTED = (
     "qemb_abi_version", "qemb_strerror", "qemb_row_stride", "qemb_quantize_rowwise",
     "qemb_dequantize", "qemb_bag_forward", "qemb_l2_error_workspace_bytes", "qemb_l2_error",
     "qemb_codebook_row_stride", "qemb_quantize_codebook", "qemb_dequantize_codebook",
-    "qemb_bag_forward_codebook", "qemb_l2_error_codebook",
+    "qemb_bag_forward_codebook", "qemb_l2_error_codebook", "qemb_interaction_width",
+    "qemb_dot_interaction",
 )
 
 CODEBOOK_ITERS = 10
@@ -74,6 +75,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.qemb_bag_forward_codebook.restype = ctypes.c_int
     L.qemb_l2_error_codebook.argtypes = [p, p, i64, i32, p, p, p]
     L.qemb_l2_error_codebook.restype = ctypes.c_int
+    L.qemb_interaction_width.argtypes = [i32, i32]
+    L.qemb_interaction_width.restype = i64
+    L.qemb_dot_interaction.argtypes = [p, p, i64, i32, i32, p, p]
+    L.qemb_dot_interaction.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -292,3 +297,35 @@ def l2_error_codebook(x: torch.Tensor, packed: torch.Tensor,
     _check("qemb_l2_error_codebook", load_library().qemb_l2_error_codebook(
         _ptr(x), _ptr(packed), rows, dim, _ptr(workspace), _ptr(out4), _stream(x)))
     return _l2_dict(out4)
+
+
+# ---- dot interaction of the pooled embeddings ----
+
+def interaction_width(T: int, dim: int) -> int:
+    w = int(load_library().qemb_interaction_width(T, dim))
+    if w < 0:
+        raise ValueError("unsupported T=%d dim=%d" % (T, dim))
+    return w
+
+
+def dot_interaction(dense: torch.Tensor, pooled: torch.Tensor,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dense [B, d], pooled [B, T, d] float32 (device) -> [B, d + T(T+1)/2]:
+    the dense vector, then the dot products of every pair of distinct rows of
+    [dense; pooled] ((1,0), (2,0), (2,1), ...)."""
+    _dev("dense", dense, torch.float32)
+    _dev("pooled", pooled, torch.float32)
+    if pooled.dim() != 3 or dense.dim() != 2:
+        raise ValueError("dense must be [B, d] and pooled [B, T, d]")
+    B, T, dim = pooled.shape
+    if tuple(dense.shape) != (B, dim):
+        raise ValueError("dense must be [%d, %d]" % (B, dim))
+    W = interaction_width(T, dim)
+    if out is None:
+        out = torch.empty((B, W), dtype=torch.float32, device=dense.device)
+    _dev("out", out, torch.float32)
+    if tuple(out.shape) != (B, W):
+        raise ValueError("out must be [%d, %d]" % (B, W))
+    _check("qemb_dot_interaction", load_library().qemb_dot_interaction(
+        _ptr(dense), _ptr(pooled), B, T, dim, _ptr(out), _stream(dense)))
+    return out

@@ -105,6 +105,58 @@ def test_l2_argument_errors(lib):
     assert e(FAKE, FAKE, 10, 16, 7, FAKE, FAKE, None) == -1
 
 
+def test_codebook_argument_errors(lib):
+    for d in (1, 2, 15, 16, 17, 64, 128, 256, 1000, 1024):
+        assert lib.qemb_codebook_row_stride(d) == oracle.codebook_row_stride(d)
+    assert lib.qemb_codebook_row_stride(0) == -1 and lib.qemb_codebook_row_stride(1025) == -1
+    qz = lib.qemb_quantize_codebook
+    assert qz(FAKE, -1, 16, 10, FAKE, None) == -1
+    assert qz(FAKE, 10, 0, 10, FAKE, None) == -1
+    assert qz(FAKE, 10, 16, -1, FAKE, None) == -1
+    assert qz(FAKE, 10, 2048, 10, FAKE, None) == -3
+    assert qz(MIS, 10, 16, 10, FAKE, None) == -2
+    assert qz(FAKE, 10, 16, 10, MIS, None) == -2
+    assert qz(None, 10, 16, 10, FAKE, None) == -1
+    assert qz(None, 0, 16, 10, None, None) == 0
+    dq = lib.qemb_dequantize_codebook
+    assert dq(FAKE, -1, 16, FAKE, None) == -1
+    assert dq(FAKE, 10, 2048, FAKE, None) == -3
+    assert dq(FAKE, 10, 16, MIS, None) == -2
+    assert dq(None, 0, 16, None, None) == 0
+    b = lib.qemb_bag_forward_codebook
+    #          packed rows toff T  B  dim idx  offs nnz itype pool  w     out   err  stream
+    assert b(FAKE, 10, FAKE, 2, 4, 16, FAKE, FAKE, 5, 2, 0, None, FAKE, None, None) == -1
+    assert b(FAKE, 10, FAKE, 2, 4, 16, FAKE, FAKE, 5, 0, 2, None, FAKE, None, None) == -1
+    assert b(FAKE, 10, FAKE, 2, 4, 16, FAKE, FAKE, 5, 0, 1, None, FAKE, None, None) == -1
+    assert b(FAKE, 10, FAKE, 2, 4, 16, FAKE, FAKE, 5, 0, 0, None, MIS, None, None) == -2
+    assert b(FAKE, 10, FAKE, 2, 4, 4096, FAKE, FAKE, 5, 0, 0, None, FAKE, None, None) == -3
+    assert b(None, 0, None, 0, 4, 16, None, None, 0, 0, 0, None, None, None, None) == 0
+    e = lib.qemb_l2_error_codebook
+    assert e(FAKE, FAKE, 10, 16, None, FAKE, None) == -1
+    assert e(FAKE, FAKE, 10, 16, MIS, FAKE, None) == -2
+    assert e(FAKE, FAKE, 10, 2048, FAKE, FAKE, None) == -3
+
+
+def test_interaction_argument_errors(lib):
+    for T, d in ((0, 1), (1, 16), (26, 64), (64, 128), (1024, 1024)):
+        assert lib.qemb_interaction_width(T, d) == oracle.interaction_width(T, d)
+    assert lib.qemb_interaction_width(-1, 16) == -1 and lib.qemb_interaction_width(1025, 16) == -1
+    assert lib.qemb_interaction_width(4, 0) == -1 and lib.qemb_interaction_width(4, 1025) == -1
+    f = lib.qemb_dot_interaction
+    #        dense pooled B  T  dim out   stream
+    assert f(FAKE, FAKE, -1, 4, 16, FAKE, None) == -1
+    assert f(FAKE, FAKE, 8, -1, 16, FAKE, None) == -1
+    assert f(FAKE, FAKE, 8, 4, 0, FAKE, None) == -1
+    assert f(FAKE, FAKE, 8, 4, 2048, FAKE, None) == -3
+    assert f(FAKE, FAKE, 8, 2000, 16, FAKE, None) == -3
+    assert f(None, FAKE, 8, 4, 16, FAKE, None) == -1
+    assert f(FAKE, None, 8, 4, 16, FAKE, None) == -1
+    assert f(FAKE, FAKE, 8, 4, 16, None, None) == -1
+    assert f(MIS, FAKE, 8, 4, 16, FAKE, None) == -2
+    assert f(FAKE, FAKE, 8, 4, 16, MIS, None) == -2
+    assert f(None, None, 0, 4, 16, None, None) == 0
+
+
 def test_binding_has_no_cpu_fallback(tmp_path):
     from int4_row_wise_amd import qemb
     saved = qemb._lib
