@@ -92,6 +92,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_bag_forward_codebook.restype = i32
         L.oracle_l2_error_codebook.argtypes = [p, p, i64, i32, p]
         L.oracle_l2_error_codebook.restype = i32
+        L.oracle_aciq_ratio.argtypes = [i32]
+        L.oracle_aciq_ratio.restype = ctypes.c_double
+        L.oracle_baseline_window.argtypes = [p, i32, i32, i32, ctypes.c_float, p]
+        L.oracle_baseline_window.restype = i32
+        L.oracle_quantize_baseline.argtypes = [p, i64, i32, i32, i32, ctypes.c_float, p]
+        L.oracle_quantize_baseline.restype = i32
         L.oracle_interaction_width.argtypes = [i32, i32]
         L.oracle_interaction_width.restype = i64
         L.oracle_dot_interaction.argtypes = [p, p, i64, i32, i32, p, p]
@@ -325,3 +331,34 @@ def dot_interaction(dense: np.ndarray, pooled: np.ndarray):
     if rc != 0:
         raise OracleError("oracle_dot_interaction returned %d" % rc)
     return out, absd
+
+
+# ---- quantizer baselines (same packed rows as quantize_rowwise) ----
+
+SYMMETRIC, PERCENTILE, ACIQ = 0, 1, 2
+
+
+def aciq_ratio(bits: int) -> float:
+    return float(lib().oracle_aciq_ratio(bits))
+
+
+def baseline_window(x_row: np.ndarray, bits: int, method: int, param: float = 0.0):
+    x_row = np.ascontiguousarray(x_row, dtype=np.float32)
+    out = np.zeros(2, dtype=np.float32)
+    rc = lib().oracle_baseline_window(_ptr(x_row), x_row.size, bits, method, param, _ptr(out))
+    if rc != 0:
+        raise OracleError("oracle_baseline_window returned %d" % rc)
+    return out[0], out[1]
+
+
+def quantize_baseline(x: np.ndarray, bits: int, method: int, param: float = 0.0) -> np.ndarray:
+    """Packed rows (the quantize_rowwise format) by a baseline method:
+    SYMMETRIC, PERCENTILE (param = p in [0.5, 1]) or ACIQ."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, dim = x.shape
+    S = row_stride(dim, bits)
+    packed = np.zeros((rows, S), dtype=np.uint8)
+    rc = lib().oracle_quantize_baseline(_ptr(x), rows, dim, bits, method, param, _ptr(packed))
+    if rc != 0:
+        raise OracleError("oracle_quantize_baseline returned %d" % rc)
+    return packed

@@ -28,6 +28,12 @@
  *    18.8%-37.5% of the fp32 size, i.e. 4-bit codes plus 16 fp32 levels per
  *    row at d = 256 and d = 64).  The clustering is 1-D Lloyd iteration from
  *    the row's uniform grid, a fixed number of times (rules below).
+ *  - Quantizer baselines the same page compares against ("Proposed method":
+ *    ACIQ, histogram-based clipping, symmetric quantization; "Main
+ *    findings": the greedy search beats them): symmetric uniform rows
+ *    (y = s q, q in [-(2^(b-1) - 1), 2^(b-1) - 1]), percentile clipping of the
+ *    row's values, and ACIQ's clipping for a Laplace prior, all stored in
+ *    the same packed row format.
  *  - Dot interaction of the pooled embeddings ("Deep Learning Recommendation
  *    Model ..." review page, "Proposed method": explicit second-order
  *    interactions are dot products between the embedding vectors and the
@@ -365,6 +371,173 @@ int oracle_quantize_rowwise(const float* x, int64_t rows, int dim, int bits,
       best_ij[2 * r + 1] = bj;
     }
     encode_row(xr, dim, bits, lo, hi, packed + r * stride, stride);
+  }
+  return bad ? OR_PRECONDITION : OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Quantizer baselines (same packed rows).                              */
+/* ------------------------------------------------------------------ */
+
+#define OR_BASE_SYMMETRIC 0
+#define OR_BASE_PERCENTILE 1
+#define OR_BASE_ACIQ 2
+
+/* ACIQ's clip ratio for M-bit codes and a Laplace(b) prior: the expected
+   squared error 2 b^2 exp(-a/b) (clipped tails) + a^2 / (3 4^M) (rounding in
+   2^M bins over [-a, a]) is smallest where (a/b) exp(a/b) = 3 4^M, i.e.
+   a/b = W(3 4^M) (Lambert W), solved here by Newton's method in binary64. */
+double oracle_aciq_ratio(int bits) {
+  double c = 3.0 * ldexp(1.0, 2 * bits);
+  double t = log(c) - log(log(c));
+  for (int it = 0; it < 100; ++it) {
+    double e = exp(t);
+    double step = (t * e - c) / (e * (t + 1.0));
+    t -= step;
+    if (fabs(step) <= 1e-16 * t) break;
+  }
+  return t;
+}
+
+/* q-quantile of ascending values v[0..d-1], linear between order statistics:
+   h = (d - 1) q, i = floor(h), v[i] + (h - i)(v[i+1] - v[i]) in binary32 with
+   one rounding for the last multiply-add. */
+static float quantile_sorted(const float* v, int d, float q) {
+  float h = (float)(d - 1) * q;
+  int i = (int)floorf(h);
+  if (i >= d - 1) return v[d - 1];
+  float f = h - (float)i;
+  return fmaf(f, v[i + 1] - v[i], v[i]);
+}
+
+/* Percentile clipping: the window is the row's (1 - p) and p quantiles. */
+static void percentile_window(const float* x, int d, float p, float* lo, float* hi) {
+  float v[OR_MAX_DIM];
+  for (int i = 0; i < d; ++i) {
+    float t = x[i];
+    int j = i;
+    while (j > 0 && v[j - 1] > t) {
+      v[j] = v[j - 1];
+      --j;
+    }
+    v[j] = t;
+  }
+  *lo = quantile_sorted(v, d, 1.0f - p) + 0.0f;
+  *hi = quantile_sorted(v, d, p) + 0.0f;
+}
+
+/* ACIQ clipping: mean mu and mean absolute deviation b of the row (each a
+   pairwise sum of the row padded with +0 to a power of two, divided by d),
+   window [mu - a, mu + a] with a = W(3 4^M) b, kept inside the row range. */
+static void aciq_window(const float* x, int d, int bits, float* lo, float* hi) {
+  float u[OR_MAX_DIM];
+  float mn, mx;
+  row_range(x, d, &mn, &mx);
+  int n = next_pow2(d);
+  for (int i = 0; i < n; ++i) u[i] = i < d ? x[i] : 0.0f;
+  float mu = pairwise_sum(u, n) / (float)d;
+  for (int i = 0; i < n; ++i) u[i] = i < d ? fabsf(x[i] - mu) : 0.0f;
+  float b = pairwise_sum(u, n) / (float)d;
+  float a = (float)oracle_aciq_ratio(bits) * b;
+  float l = mu - a, h = mu + a;
+  *lo = (l > mn ? l : mn) + 0.0f;
+  *hi = (h < mx ? h : mx) + 0.0f;
+}
+
+/* Symmetric uniform row: s = max|x| / (2^(b-1) - 1) stored in binary16 (at
+   most 65504 / 2^(b-1), so that the bias stays finite), q = rint(x / s)
+   (times the reciprocal of the stored scale) clamped to [-(2^(b-1) - 1),
+   2^(b-1) - 1]; stored as code q + 2^(b-1) with bias -2^(b-1) s (exact), so
+   the unchanged decode fmaf(s, code, bias) gives s q exactly. */
+static void encode_symmetric(const float* x, int d, int bits, uint8_t* row, int64_t stride) {
+  int H = 1 << (bits - 1), Qs = H - 1;
+  float m = 0.0f;
+  for (int i = 0; i < d; ++i) {
+    float a = fabsf(x[i]);
+    if (a > m) m = a;
+  }
+  float s = m / (float)Qs;
+  uint16_t s16 = to_half(s);
+  float sf = from_half(s16);
+  float smax = 65504.0f / (float)H;
+  if (sf > smax) {
+    s16 = to_half(smax);
+    sf = smax;
+  }
+  uint16_t b16 = to_half(-(float)H * sf);
+  float r = sf == 0.0f ? 0.0f : 1.0f / sf;
+  int64_t C = code_bytes(d, bits);
+  memset(row, 0, (size_t)stride);
+  for (int i = 0; i < d; ++i) {
+    float q = sf == 0.0f ? 0.0f : rintf(x[i] * r);
+    if (q < -(float)Qs) q = -(float)Qs;
+    if (q > (float)Qs) q = (float)Qs;
+    int c = (int)q + H;
+    if (bits == 8) {
+      row[i] = (uint8_t)c;
+    } else if ((i & 1) == 0) {
+      row[i / 2] = (uint8_t)(row[i / 2] | c);
+    } else {
+      row[i / 2] = (uint8_t)(row[i / 2] | (c << 4));
+    }
+  }
+  row[C + 0] = (uint8_t)(s16 & 0xff);
+  row[C + 1] = (uint8_t)(s16 >> 8);
+  row[C + 2] = (uint8_t)(b16 & 0xff);
+  row[C + 3] = (uint8_t)(b16 >> 8);
+}
+
+/* The window a baseline picks for one row (symmetric: [-max|x|, max|x|]). */
+int oracle_baseline_window(const float* x, int dim, int bits, int method, float param,
+                           float* lo_hi) {
+  if (dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  float lo, hi;
+  if (method == OR_BASE_SYMMETRIC) {
+    float m = 0.0f;
+    for (int i = 0; i < dim; ++i) m = fabsf(x[i]) > m ? fabsf(x[i]) : m;
+    lo = -m;
+    hi = m;
+  } else if (method == OR_BASE_PERCENTILE) {
+    if (!(param >= 0.5f && param <= 1.0f)) return OR_INVALID;
+    percentile_window(x, dim, param, &lo, &hi);
+  } else if (method == OR_BASE_ACIQ) {
+    aciq_window(x, dim, bits, &lo, &hi);
+  } else {
+    return OR_INVALID;
+  }
+  lo_hi[0] = lo;
+  lo_hi[1] = hi;
+  return OR_OK;
+}
+
+/* method: OR_BASE_SYMMETRIC, OR_BASE_PERCENTILE (param = p in [0.5, 1]) or
+   OR_BASE_ACIQ; rows in the packed format of oracle_quantize_rowwise. */
+int oracle_quantize_baseline(const float* x, int64_t rows, int dim, int bits, int method,
+                             float param, uint8_t* packed) {
+  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  if (method < OR_BASE_SYMMETRIC || method > OR_BASE_ACIQ) return OR_INVALID;
+  if (method == OR_BASE_PERCENTILE && !(param >= 0.5f && param <= 1.0f)) return OR_INVALID;
+  int64_t stride = oracle_row_stride(dim, bits);
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + r * (int64_t)dim;
+    if (!row_precondition_ok(xr, dim)) {
+      bad = 1;
+      continue;
+    }
+    uint8_t* row = packed + r * stride;
+    if (method == OR_BASE_SYMMETRIC) {
+      encode_symmetric(xr, dim, bits, row, stride);
+    } else {
+      float lo, hi;
+      if (method == OR_BASE_PERCENTILE) {
+        percentile_window(xr, dim, param, &lo, &hi);
+      } else {
+        aciq_window(xr, dim, bits, &lo, &hi);
+      }
+      encode_row(xr, dim, bits, lo, hi, row, stride);
+    }
   }
   return bad ? OR_PRECONDITION : OR_OK;
 }

@@ -219,3 +219,74 @@ def encode_codebook(x, n_iter=10):
     qq[:d] = q
     row[64:64 + C] = (qq[0::2] | (qq[1::2] << 4)).astype(np.uint8)
     return row
+
+
+# ---- quantizer baselines: symmetric, percentile clipping, ACIQ ----
+
+def encode_symmetric(x, bits):
+    """Symmetric row: s = max|x| / (2^(b-1) - 1) in fp16 (capped at
+    65504 / 2^(b-1)), codes rint(x * (1/s)) clamped to +-(2^(b-1) - 1) and
+    stored + 2^(b-1), bias -2^(b-1) s."""
+    x = np.asarray(x, dtype=np.float32)
+    H = 1 << (bits - 1)
+    m = F32(np.max(np.abs(x)))
+    sf = half(m / F32(H - 1))
+    if sf > F32(65504.0 / H):
+        sf = F32(65504.0 / H)
+    s16 = half_bits(sf)
+    b16 = half_bits(F32(-H) * sf)
+    if sf == 0:
+        q = np.zeros(x.size, dtype=np.int64)
+    else:
+        r = F32(1.0) / sf
+        q = np.clip(np.rint((x * r).astype(np.float32)), -(H - 1), H - 1).astype(np.int64)
+    return _pack(q + H, bits, s16, b16)
+
+
+def _pack(codes, bits, s16, b16):
+    d = codes.size
+    C = (d * bits + 7) // 8
+    S = (C + 4 + 15) // 16 * 16
+    row = np.zeros(S, dtype=np.uint8)
+    if bits == 8:
+        row[:d] = codes
+    else:
+        qq = np.zeros(2 * C, dtype=np.int64)
+        qq[:d] = codes
+        row[:C] = (qq[0::2] | (qq[1::2] << 4)).astype(np.uint8)
+    row[C:C + 2] = [s16 & 0xFF, s16 >> 8]
+    row[C + 2:C + 4] = [b16 & 0xFF, b16 >> 8]
+    return row
+
+
+def percentile_window(x, p):
+    v = np.sort(np.asarray(x, dtype=np.float32), kind="stable")
+    d = v.size
+
+    def qnt(q):
+        h = F32(d - 1) * F32(q)
+        i = int(np.floor(h))
+        if i >= d - 1:
+            return F32(v[d - 1])
+        f = F32(h - F32(i))
+        return F32(fma32(float(f), float(F32(v[i + 1] - v[i])), float(v[i])))
+
+    return qnt(F32(1.0) - F32(p)) + F32(0.0), qnt(p) + F32(0.0)
+
+
+def aciq_window(x, bits, ratio):
+    """ratio: the clip ratio a/b as a float32."""
+    x = np.asarray(x, dtype=np.float32)
+    mn, mx = row_range(x)
+    mu = F32(pairwise(x) / F32(x.size))
+    b = F32(pairwise(np.abs((x - mu).astype(np.float32))) / F32(x.size))
+    a = F32(F32(ratio) * b)
+    lo, hi = F32(mu - a), F32(mu + a)
+    return max(lo, mn) + F32(0.0), min(hi, mx) + F32(0.0)
+
+
+def encode_window(x, bits, lo, hi):
+    x = np.asarray(x, dtype=np.float32)
+    Q = (1 << bits) - 1
+    s16, b16, sf, bf = params(lo, hi, Q)
+    return _pack(codes(x, sf, bf, Q), bits, s16, b16)
