@@ -316,6 +316,20 @@ def quantizer_extras(q, synth, torch, dev, reps=3):
     res["codebook_quantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3, "n_iter": q.CODEBOOK_ITERS,
                                 "bytes_per_row": cb.shape[1]}
     res["codebook_l2"] = q.l2_error_codebook(x, cb)
+    # the baselines the greedy search is compared with, same packed format
+    pk = torch.empty((rows, S), dtype=torch.uint8, device=dev)
+    for name, method, param in (("symmetric", q.SYMMETRIC, 0.0), ("percentile_0.99", q.PERCENTILE, 0.99),
+                                ("aciq", q.ACIQ, 0.0)):
+        ms = timed(lambda: q.quantize_baseline(x, 4, method, param, out=pk), 1)
+        res["baseline_" + name] = {"ms": ms, "rows_per_s": rows / ms * 1e3,
+                                   "GBps": (in_b + out_b) / ms / 1e6,
+                                   "hbm_frac": (in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS,
+                                   "l2": q.l2_error(x, pk, 4)}
+    del pk
+    res["l2_mean_row_by_method"] = {
+        k: res[k]["mean_row"] for k in ("codebook_l2", "greedy_l2", "range_l2")} | {
+        "baseline_" + n + "_l2": res["baseline_" + n]["l2"]["mean_row"]
+        for n in ("symmetric", "percentile_0.99", "aciq")}
     cb_out = rows * cb.shape[1]
     ms = timed(lambda: q.dequantize_codebook(cb, dim, out=y), reps)
     res["codebook_dequantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3,

@@ -87,6 +87,10 @@ typedef struct ihipStream_t* qemb_stream_t; /* the same type as hipStream_t */
 #define QEMB_CLIP_RANGE 0
 #define QEMB_CLIP_GREEDY 1
 
+#define QEMB_BASE_SYMMETRIC 0
+#define QEMB_BASE_PERCENTILE 1
+#define QEMB_BASE_ACIQ 2
+
 #define QEMB_POOL_SUM 0
 #define QEMB_POOL_WEIGHTED_SUM 1
 
@@ -120,6 +124,32 @@ int64_t qemb_row_stride(int32_t dim, int32_t bits);
 int qemb_quantize_rowwise(const float* x, int64_t rows, int32_t dim, int32_t bits,
                           int32_t clip_mode, int32_t n_bins, int32_t n_steps,
                           uint8_t* packed, qemb_stream_t stream);
+
+/*
+ * Quantizer baselines the same page compares the greedy search against
+ * ("Proposed method": ACIQ, histogram-based clipping, symmetric
+ * quantization; "Main findings"), writing the packed rows of
+ * qemb_quantize_rowwise, so qemb_dequantize and qemb_bag_forward read them
+ * unchanged.  Bit-exact, deterministic.
+ *   QEMB_BASE_SYMMETRIC   y = s q, q in [-(2^(bits-1) - 1), 2^(bits-1) - 1],
+ *       s = max|x| / (2^(bits-1) - 1) rounded to fp16 and capped at
+ *       65504 / 2^(bits-1); q = rint(x * (1/s)) clamped; stored as code
+ *       q + 2^(bits-1) with bias -2^(bits-1) s (exact), so y = s q exactly
+ *   QEMB_BASE_PERCENTILE  window [Q(1 - p), Q(p)] of the row's values, p =
+ *       param in [0.5, 1]; Q(q): h = (dim - 1) q (fp32), i = floor(h), the
+ *       i-th smallest value v_i (ties in position order), Q = fmaf(h - i,
+ *       v_{i+1} - v_i, v_i) (Q = v_{dim-1} when i >= dim - 1); then encoded as
+ *       the range rule does for [lo, hi]
+ *   QEMB_BASE_ACIQ  window [max(min, mu - a), min(max, mu + a)], mu = the
+ *       row mean, b = mean |x - mu| (each a contiguous-halves pairwise fp32
+ *       sum of the row padded with +0 to a power of two, divided by dim),
+ *       a = t b with t = W(3 * 4^bits) as fp32 (Lambert W: the clip that
+ *       minimizes the clipping plus rounding error of a Laplace(b) source)
+ *   x, rows, dim, bits, packed: as qemb_quantize_rowwise; param ignored
+ *   except for PERCENTILE.
+ */
+int qemb_quantize_baseline(const float* x, int64_t rows, int32_t dim, int32_t bits, int32_t method,
+                           float param, uint8_t* packed, qemb_stream_t stream);
 
 /*
  * Decode packed rows to fp32: y[r][k] = fmaf(scale_r, code_rk, bias_r)

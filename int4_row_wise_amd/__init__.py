@@ -7,7 +7,8 @@ library loads on first use and raises if it was not built; there is no CPU
 fallback.  :mod:`int4_row_wise_amd.synth` draws the seeded synthetic inputs.
 """
 from .qemb import (  # noqa: F401
-    RANGE, GREEDY, SUM, WEIGHTED_SUM, CODEBOOK_ITERS, QembError, abi_version, bag_forward,
+    RANGE, GREEDY, SUM, WEIGHTED_SUM, CODEBOOK_ITERS, SYMMETRIC, PERCENTILE, ACIQ, QembError,
+    abi_version, bag_forward, quantize_baseline,
     bag_forward_codebook, codebook_row_stride, dequantize, dequantize_codebook, dot_interaction,
     interaction_width, l2_error,
     l2_error_codebook, load_library, quantize_codebook, quantize_rowwise, row_stride,

@@ -1407,6 +1407,201 @@ __global__ __launch_bounds__(kBlock) void l2_final_kernel(const double* __restri
 }
 
 // ---------------------------------------------------------------------------
+// quantizer baselines ("Post-Training 4-bit Quantization on Embedding
+// Tables", review page, "Proposed method": the comparison with symmetric
+// quantization, histogram-based clipping and ACIQ), in the packed row format:
+//   SYMMETRIC   y = s q, q in [-(2^(b-1) - 1), 2^(b-1) - 1], s = max|x| /
+//               (2^(b-1) - 1) in fp16 (at most 65504 / 2^(b-1)); stored as
+//               code q + 2^(b-1) with bias -2^(b-1) s (exact in fp16)
+//   PERCENTILE  window = the row's (1 - p) and p quantiles, linear between
+//               order statistics (h = (d - 1) q, fmaf(h - i, v[i+1] - v[i], v[i]))
+//   ACIQ        window = mean +- W(3 4^b) * mean|x - mean| (Laplace prior),
+//               inside the row range; both means are pairwise sums of the row
+//               padded with +0 to a power of two, divided by d
+// LPR lanes per row, EPL contiguous elements per lane (the row padded with
+// +0 to P = EPL * LPR, a power of two), so a lane's pairwise sum followed by
+// xor butterflies is the contiguous-halves pairwise sum of the padded row.
+// ---------------------------------------------------------------------------
+
+constexpr int kBaseSym = 0, kBasePct = 1, kBaseAciq = 2;
+
+// W(3 4^b) as binary32: 5.0286403 (b = 4), 9.8967600 (b = 8)
+template <int BITS>
+__device__ __forceinline__ float aciq_ratio() {
+  return __builtin_bit_cast(float, BITS == 4 ? 0x40a0ea9fu : 0x411e5921u);
+}
+
+template <int EPL, int LPR>
+__device__ __forceinline__ float lane_pairwise_group_sum(const float (&u0)[EPL]) {
+  float u[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) u[e] = u0[e];
+#pragma unroll
+  for (int h = 1; h < EPL; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 2 * h) u[e] = u[e] + u[e + h];
+  }
+  float t = u[0];
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) t = t + __shfl_xor(t, m);
+  return t;
+}
+
+template <int LPR>
+__device__ __forceinline__ uint32_t group_or(uint32_t v) {
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) v |= (uint32_t)__shfl_xor((int)v, m);
+  return v;
+}
+
+template <int BITS, int EPL, int LPR, int METHOD>
+__global__ __launch_bounds__(kBlock) void quantize_baseline_kernel(
+    const float* __restrict__ x, int64_t rows, int dim, int C, int S, int vec4, float param,
+    uint8_t* __restrict__ packed) {
+  constexpr int H = 1 << (BITS - 1), Qs = H - 1;
+  const int s = threadIdx.x % LPR;
+  const int64_t groups = (int64_t)gridDim.x * (kBlock / LPR);
+  for (int64_t row = (int64_t)blockIdx.x * (kBlock / LPR) + threadIdx.x / LPR; row < rows;
+       row += groups) {
+    const float* xr = x + row * dim;
+    const int e0 = s * EPL;
+    const int valid = min(max(dim - e0, 0), EPL);
+    float v[EPL];
+    if (EPL >= 4 && vec4 && valid == EPL) {
+#pragma unroll
+      for (int k = 0; k < EPL; k += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(xr + e0 + k);
+        v[k] = a.x; v[k + 1] = a.y; v[k + 2] = a.z; v[k + 3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) v[k] = (k < valid) ? xr[e0 + k] : 0.0f;
+    }
+    uint32_t s16, b16;
+    float sf, bf, r;
+    if constexpr (METHOD == kBaseSym) {
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k)
+        if (k < valid) m = fmaxf(m, __builtin_fabsf(v[k]));
+      m = group_max<LPR>(m);
+      s16 = half_bits(m / (float)Qs);
+      sf = half_value(s16);
+      constexpr float smax = 65504.0f / (float)H;
+      if (sf > smax) {
+        s16 = half_bits(smax);
+        sf = smax;
+      }
+      // the product stays an fp32 multiply: fused into the fp16 conversion it
+      // became v_fma_mix with a +0 addend, which turns -8 * (+0) into +0
+      float nb = -(float)H * sf;
+      asm volatile("" : "+v"(nb));
+      b16 = half_bits(nb);
+      bf = half_value(b16);
+      r = sf == 0.0f ? 0.0f : 1.0f / sf;
+    } else {
+      float lo, hi;
+      float mn = __builtin_inff(), mx = -__builtin_inff();
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        if (k < valid) {
+          mn = fminf(mn, v[k]);
+          mx = fmaxf(mx, v[k]);
+        }
+      }
+      mn = group_min<LPR>(mn) + 0.0f;
+      mx = group_max<LPR>(mx) + 0.0f;
+      if constexpr (METHOD == kBaseAciq) {
+        float u[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) u[k] = k < valid ? v[k] : 0.0f;
+        const float mu = lane_pairwise_group_sum<EPL, LPR>(u) / (float)dim;
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) u[k] = k < valid ? __builtin_fabsf(v[k] - mu) : 0.0f;
+        const float bsc = lane_pairwise_group_sum<EPL, LPR>(u) / (float)dim;
+        const float a = aciq_ratio<BITS>() * bsc;
+        const float l = mu - a, h = mu + a;
+        lo = (l > mn ? l : mn) + 0.0f;
+        hi = (h < mx ? h : mx) + 0.0f;
+      } else {
+        // ranks by value, ties by position: the order of a stable sort
+        int rk[EPL];
+#pragma unroll
+        for (int k = 0; k < EPL; ++k) rk[k] = 0;
+        const int gbase = (threadIdx.x % kWave) - s;
+        for (int t = 0; t < LPR; ++t) {
+#pragma unroll
+          for (int kk = 0; kk < EPL; ++kk) {
+            const float o = __shfl(v[kk], gbase + t);
+            const int j = t * EPL + kk;
+#pragma unroll
+            for (int k = 0; k < EPL; ++k) {
+              const int i = e0 + k;
+              rk[k] += (j < dim && (o < v[k] || (o == v[k] && j < i))) ? 1 : 0;
+            }
+          }
+        }
+        auto order_stat = [&](int want) {
+          uint32_t b = 0u;
+#pragma unroll
+          for (int k = 0; k < EPL; ++k)
+            b |= (k < valid && rk[k] == want) ? __builtin_bit_cast(uint32_t, v[k]) : 0u;
+          return __builtin_bit_cast(float, group_or<LPR>(b));
+        };
+        auto quantile = [&](float q) {
+          const float hq = (float)(dim - 1) * q;
+          const int i = (int)__builtin_floorf(hq);
+          if (i >= dim - 1) return order_stat(dim - 1);
+          const float f = hq - (float)i;
+          const float v0 = order_stat(i), v1 = order_stat(i + 1);
+          return __builtin_fmaf(f, v1 - v0, v0);
+        };
+        lo = quantile(1.0f - param) + 0.0f;
+        hi = quantile(param) + 0.0f;
+      }
+      const Window w = make_window<BITS>(lo, hi);
+      s16 = w.s16;
+      b16 = w.b16;
+      sf = w.sf;
+      bf = w.bf;
+      r = w.r;
+    }
+    // codes of this lane's elements (padding elements 0)
+    constexpr int LW = (EPL * BITS + 31) / 32;  // code words of one lane
+    uint32_t cw[LW];
+#pragma unroll
+    for (int j = 0; j < LW; ++j) cw[j] = 0u;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      if (k < valid) {
+        uint32_t q;
+        if constexpr (METHOD == kBaseSym) {
+          const float t = sf == 0.0f ? 0.0f : __builtin_rintf(v[k] * r);
+          q = (uint32_t)(int)(fminf(fmaxf(t, -(float)Qs), (float)Qs) + (float)H);
+        } else {
+          constexpr float Qf = (float)((1 << BITS) - 1);
+          q = (uint32_t)fminf(fmaxf(__builtin_rintf((v[k] - bf) * r), 0.0f), Qf);
+        }
+        cw[(k * BITS) / 32] |= q << ((k * BITS) % 32);
+      }
+    }
+    (void)bf;
+    const uint32_t p32 = s16 | (b16 << 16);
+    uint8_t* prow = packed + row * (int64_t)S;
+    const int nwords = S / 4;
+    // the lane's own words, then the words past every lane's codes (scale,
+    // bias and padding) round robin
+#pragma unroll
+    for (int j = 0; j < LW; ++j) {
+      const int wd = s * LW + j;
+      if (wd < nwords) *reinterpret_cast<uint32_t*>(prow + 4 * wd) = cw[j] | param_part(p32, C - 4 * wd);
+    }
+    for (int wd = LPR * LW + s; wd < nwords; wd += LPR)
+      *reinterpret_cast<uint32_t*>(prow + 4 * wd) = param_part(p32, C - 4 * wd);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // codebook rows: 16 fp32 levels per row (1-D k-means), 4-bit codes
 // ("Post-Training 4-bit Quantization on Embedding Tables", review page,
 // "Proposed method": codebook quantization by k-means clustering; "Main
@@ -2323,6 +2518,43 @@ int dispatch_wave(const BagArgs& a, hipStream_t st) {
 // C ABI
 // ---------------------------------------------------------------------------
 
+template <int BITS, int EPL, int LPR, int METHOD>
+int launch_baseline(const float* x, int64_t rows, int dim, int C, int S, int vec4, float param,
+                    uint8_t* packed, hipStream_t st) {
+  hipLaunchKernelGGL((quantize_baseline_kernel<BITS, EPL, LPR, METHOD>),
+                     dim3(grid_for(rows, kBlock / LPR, kGridCap)), dim3(kBlock), 0, st, x, rows, dim,
+                     C, S, vec4, param, packed);
+  return launched();
+}
+
+template <int BITS, int METHOD>
+int baseline_by_dim(const float* x, int64_t rows, int dim, int C, int S, int vec4, float param,
+                    uint8_t* packed, hipStream_t st) {
+  switch (next_pow2(dim)) {
+    case 1: return launch_baseline<BITS, 1, 1, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    case 2: return launch_baseline<BITS, 2, 1, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    case 4: return launch_baseline<BITS, 4, 1, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    case 8: return launch_baseline<BITS, 8, 1, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    case 16: return launch_baseline<BITS, 16, 1, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    case 32: return launch_baseline<BITS, 16, 2, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    case 64: return launch_baseline<BITS, 16, 4, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    case 128: return launch_baseline<BITS, 16, 8, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    case 256: return launch_baseline<BITS, 16, 16, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    case 512: return launch_baseline<BITS, 16, 32, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+    default: return launch_baseline<BITS, 16, 64, METHOD>(x, rows, dim, C, S, vec4, param, packed, st);
+  }
+}
+
+template <int BITS>
+int baseline_by_method(int method, const float* x, int64_t rows, int dim, int C, int S, int vec4,
+                       float param, uint8_t* packed, hipStream_t st) {
+  if (method == QEMB_BASE_SYMMETRIC)
+    return baseline_by_dim<BITS, kBaseSym>(x, rows, dim, C, S, vec4, param, packed, st);
+  if (method == QEMB_BASE_PERCENTILE)
+    return baseline_by_dim<BITS, kBasePct>(x, rows, dim, C, S, vec4, param, packed, st);
+  return baseline_by_dim<BITS, kBaseAciq>(x, rows, dim, C, S, vec4, param, packed, st);
+}
+
 template <int EPL, int LPR>
 int launch_codebook(const float* x, int64_t rows, int dim, int S, int vec4, int n_iter,
                     uint8_t* packed, hipStream_t st) {
@@ -2492,6 +2724,23 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
 }
 
 size_t qemb_l2_error_workspace_bytes(void) { return (size_t)kL2Blocks * 4 * sizeof(double); }
+
+int qemb_quantize_baseline(const float* x, int64_t rows, int32_t dim, int32_t bits, int32_t method,
+                           float param, uint8_t* packed, qemb_stream_t stream) {
+  if (rows < 0 || dim < 1 || (bits != 4 && bits != 8)) return QEMB_E_INVALID_ARG;
+  if (method != QEMB_BASE_SYMMETRIC && method != QEMB_BASE_PERCENTILE && method != QEMB_BASE_ACIQ)
+    return QEMB_E_INVALID_ARG;
+  if (method == QEMB_BASE_PERCENTILE && !(param >= 0.5f && param <= 1.0f)) return QEMB_E_INVALID_ARG;
+  if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
+  if (rows == 0) return QEMB_OK;
+  if (!x || !packed) return QEMB_E_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(packed)) return QEMB_E_MISALIGNED;
+  const int C = (int)code_bytes(dim, bits), S = (int)qemb_row_stride(dim, bits);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int vec4 = dim % 4 == 0;
+  return bits == 4 ? baseline_by_method<4>(method, x, rows, dim, C, S, vec4, param, packed, st)
+                   : baseline_by_method<8>(method, x, rows, dim, C, S, vec4, param, packed, st);
+}
 
 int64_t qemb_codebook_row_stride(int32_t dim) {
   if (dim < 1 || dim > QEMB_MAX_DIM) return -1;

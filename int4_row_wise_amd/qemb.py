@@ -27,8 +27,10 @@ EXPORTED = (
     "qemb_dequantize", "qemb_bag_forward", "qemb_l2_error_workspace_bytes", "qemb_l2_error",
     "qemb_codebook_row_stride", "qemb_quantize_codebook", "qemb_dequantize_codebook",
     "qemb_bag_forward_codebook", "qemb_l2_error_codebook", "qemb_interaction_width",
-    "qemb_dot_interaction",
+    "qemb_dot_interaction", "qemb_quantize_baseline",
 )
+
+SYMMETRIC, PERCENTILE, ACIQ = 0, 1, 2
 
 CODEBOOK_ITERS = 10
 
@@ -75,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.qemb_bag_forward_codebook.restype = ctypes.c_int
     L.qemb_l2_error_codebook.argtypes = [p, p, i64, i32, p, p, p]
     L.qemb_l2_error_codebook.restype = ctypes.c_int
+    L.qemb_quantize_baseline.argtypes = [p, i64, i32, i32, i32, ctypes.c_float, p, p]
+    L.qemb_quantize_baseline.restype = ctypes.c_int
     L.qemb_interaction_width.argtypes = [i32, i32]
     L.qemb_interaction_width.restype = i64
     L.qemb_dot_interaction.argtypes = [p, p, i64, i32, i32, p, p]
@@ -135,6 +139,23 @@ def quantize_rowwise(x: torch.Tensor, bits: int = 4, clip_mode=RANGE, n_bins: in
         raise ValueError("out must be [%d, %d]" % (rows, S))
     _check("qemb_quantize_rowwise", load_library().qemb_quantize_rowwise(
         _ptr(x), rows, dim, bits, _clip(clip_mode), n_bins, n_steps, _ptr(out), _stream(x)))
+    return out
+
+
+def quantize_baseline(x: torch.Tensor, bits: int = 4, method: int = SYMMETRIC, param: float = 0.0,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Baseline quantizers in the packed row format: SYMMETRIC, PERCENTILE
+    (param = p in [0.5, 1]) or ACIQ.  x [rows, dim] float32 (device)."""
+    _dev("x", x, torch.float32)
+    rows, dim = x.shape
+    S = row_stride(dim, bits)
+    if out is None:
+        out = torch.empty((rows, S), dtype=torch.uint8, device=x.device)
+    _dev("out", out, torch.uint8)
+    if tuple(out.shape) != (rows, S):
+        raise ValueError("out must be [%d, %d]" % (rows, S))
+    _check("qemb_quantize_baseline", load_library().qemb_quantize_baseline(
+        _ptr(x), rows, dim, bits, int(method), float(param), _ptr(out), _stream(x)))
     return out
 
 

@@ -166,3 +166,17 @@ def test_binding_has_no_cpu_fallback(tmp_path):
             qemb.load_library(str(tmp_path / "missing.so"))
     finally:
         qemb._lib = saved
+
+
+def test_baseline_argument_errors(lib):
+    f = lib.qemb_quantize_baseline
+    #        x     rows dim bits meth param packed stream
+    assert f(FAKE, -1, 16, 4, 0, 0.0, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 5, 0, 0.0, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 4, 3, 0.0, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 4, 1, 0.4, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 4, 1, 1.5, FAKE, None) == -1
+    assert f(FAKE, 10, 2048, 4, 0, 0.0, FAKE, None) == -3
+    assert f(MIS, 10, 16, 4, 0, 0.0, FAKE, None) == -2
+    assert f(FAKE, 10, 16, 4, 0, 0.0, MIS, None) == -2
+    assert f(None, 0, 16, 4, 2, 0.0, None, None) == 0

@@ -10,6 +10,9 @@ cross-compiles the device code to text).
   uniform 64-bit comparisons are routed around (uniform_flag in the source).
 - Every v_permlane16/32_swap follows an s_nop 3: the swaps are issued from
   inline asm, which gets no hazard wait states from the compiler.
+- No v_fma_mixlo/mixhi_f16 adds a literal +0: the compiler forms that from
+  an fp32 multiply followed by a conversion to fp16, and x * y + 0 turns a
+  product of -0 into +0.
 """
 from __future__ import annotations
 
@@ -84,4 +87,10 @@ def test_swaps_have_wait_states(asm):
     swaps = [i for i, l in enumerate(lines) if l.startswith(("v_permlane16_swap", "v_permlane32_swap"))]
     assert swaps, "the lookup's reduce-scatter should use the swaps"
     bad = [lines[i] for i in swaps if lines[i - 1] != "s_nop 3"]
+    assert not bad, bad[:5]
+
+
+def test_no_fp16_mix_fma_with_plus_zero_addend(asm):
+    pat = re.compile(r"\s*v_fma_mix(lo|hi)_f16\s+\S+,\s*\S+,\s*\S+,\s*0\s*$")
+    bad = [l.strip() for l in instructions(asm) if pat.match(l)]
     assert not bad, bad[:5]
