@@ -73,9 +73,9 @@ def check_sampled_rows(q, w, packed, bits, omode, n_samples, seed):
         assert np.array_equal(got, ref), "table %d: %d rows differ" % (t, int((got != ref).any(1).sum()))
 
 
-def check_sampled_bags(q, w, packed_gpu, bits, omode, bt, out, n_bags, seed):
+def check_sampled_bags(q, w, packed_gpu, bits, omode, bt, out, n_bags, seed, codebook=False):
     """Recompute n_bags sampled bags with the oracle over oracle-packed copies
-    of exactly the rows they reference."""
+    of exactly the rows they reference (codebook: oracle codebook rows)."""
     g = np.random.default_rng(seed)
     G = bt.T * bt.B
     bags = np.unique(np.concatenate([[0, G - 1], g.integers(0, G, size=n_bags)]))
@@ -92,7 +92,8 @@ def check_sampled_bags(q, w, packed_gpu, bits, omode, bt, out, n_bags, seed):
     for t, gbs in sorted(by_table.items()):
         ids_t = np.unique(np.concatenate([idx[offs[gb]:offs[gb + 1]] for gb in gbs]))
         x = fp32_rows(w, t, ids_t)
-        mini_rows.append(oracle.quantize_rowwise(x, bits, omode, w.n_bins, w.n_steps))
+        mini_rows.append(oracle.quantize_codebook(x) if codebook else
+                         oracle.quantize_rowwise(x, bits, omode, w.n_bins, w.n_steps))
         remap = {int(r): row_base + i for i, r in enumerate(ids_t)}
         for gb in gbs:
             sl = slice(offs[gb], offs[gb + 1])
@@ -104,10 +105,14 @@ def check_sampled_bags(q, w, packed_gpu, bits, omode, bt, out, n_bags, seed):
         row_base += ids_t.size
     mini = np.concatenate(mini_rows)
     nb = len(order)
-    ref, absd, err = oracle.bag_forward(
-        mini, np.array([0, mini.shape[0]], np.int64), nb, w.dim, bits,
-        np.array(sub_ids, np.int64), np.array(sub_offs, np.int64),
-        np.array(sub_w, np.float32) if bt.weights is not None else None)
+    args = (np.array(sub_ids, np.int64), np.array(sub_offs, np.int64),
+            np.array(sub_w, np.float32) if bt.weights is not None else None)
+    if codebook:
+        ref, absd, err = oracle.bag_forward_codebook(
+            mini, np.array([0, mini.shape[0]], np.int64), nb, w.dim, *args)
+    else:
+        ref, absd, err = oracle.bag_forward(
+            mini, np.array([0, mini.shape[0]], np.int64), nb, w.dim, bits, *args)
     assert err == 0
     order = np.array(order)
     got = out[order % bt.B, order // bt.B, :]
@@ -194,4 +199,78 @@ def test_quantizer_workload_full(q):
         full = q.l2_error(x, packed, 4)
         assert full["rows"] == rows and 0.05 < full["mean_row"] < 0.2
         del packed
+    torch.cuda.empty_cache()
+
+
+def test_codebook_multi_hot_full(q):
+    """The multi-hot workload over codebook rows (64 tables x 1M rows, d=128,
+    10 k-means iterations per row) -- the benchmarked codebook call."""
+    import torch
+    w = synth.workload(4)
+    print("codebook multi-hot full size", flush=True)
+    S = q.codebook_row_stride(w.dim)
+    packed = torch.empty((w.total_rows, S), dtype=torch.uint8, device="cuda")
+    r0 = 0
+    for t in range(w.n_tables):
+        x = synth.table_values_torch(w, t, 0, w.rows[t], "cuda")
+        q.quantize_codebook(x, out=packed[r0:r0 + w.rows[t]])
+        del x
+        r0 += w.rows[t]
+    g = np.random.default_rng(90)
+    toff = np.concatenate([[0], np.cumsum(w.rows)])
+    for t in np.unique(g.integers(0, w.n_tables, size=12)):
+        rows = np.unique(np.concatenate([[0, w.rows[t] - 1], g.integers(0, w.rows[t], size=200)]))
+        ref = oracle.quantize_codebook(fp32_rows(w, int(t), rows))
+        assert np.array_equal(host(packed[dev(toff[t] + rows)]), ref), "table %d" % t
+    bt = synth.batch(w, batch_seed=0, index_dtype=np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = host(q.bag_forward_codebook(packed, dev(bt.table_offsets), bt.B, w.dim, dev(bt.indices),
+                                      dev(bt.offsets), dev(bt.weights), err_count=err))
+    assert int(host(err)[0]) == 0
+    check_sampled_bags(q, w, packed, 4, None, bt, out, 400, 91, codebook=True)
+    assert np.isfinite(out).all()
+
+
+def test_interaction_full(q):
+    """The dot interaction at the multi-hot batch (16384 samples x 64 pooled
+    vectors of d=128, the benchmarked launch) on seeded synthetic inputs;
+    sampled samples against the oracle."""
+    import torch
+    print("interaction full size", flush=True)
+    B, T, d = 16384, 64, 128
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(12)
+    pooled = torch.randn((B, T, d), generator=gen, device="cuda") * 0.1
+    dense = torch.randn((B, d), generator=gen, device="cuda")
+    out = host(q.dot_interaction(dense, pooled))
+    g = np.random.default_rng(92)
+    smp = np.unique(np.concatenate([[0, B - 1], g.integers(0, B, size=300)]))
+    ref, absd = oracle.dot_interaction(host(dense[dev(smp)]), host(pooled[dev(smp)]))
+    got = out[smp]
+    assert np.array_equal(got[:, :d].astype(np.float64), ref[:, :d])
+    err = np.abs(got[:, d:].astype(np.float64) - ref[:, d:])
+    assert np.all(err <= d * 2.0 ** -23 * absd[:, d:] + 1e-37)
+    out2 = host(q.dot_interaction(dense, pooled))
+    assert np.array_equal(out.view(np.uint32), out2.view(np.uint32))
+
+
+def test_baselines_quantizer_workload_full(q):
+    """The 5e7 x 64 quantizer table through the three baselines; sampled rows
+    bit-exact against the oracle on re-drawn values."""
+    import torch
+    w = synth.workload(5)
+    print("baselines on the quantizer workload, full size", flush=True)
+    rows = w.rows[0]
+    x = synth.table_values_torch(w, 0, 0, rows, "cuda")
+    g = np.random.default_rng(93)
+    sample = np.unique(np.concatenate([[0, rows - 1], g.integers(0, rows, size=2000)]))
+    xs = fp32_rows(w, 0, sample)
+    for method, param in ((q.SYMMETRIC, 0.0), (q.PERCENTILE, 0.99), (q.ACIQ, 0.0)):
+        packed = q.quantize_baseline(x, 4, method, param)
+        ref = oracle.quantize_baseline(xs, 4, method, param)
+        assert np.array_equal(host(packed[dev(sample)]), ref), method
+        del packed
+    cb = q.quantize_codebook(x)
+    assert np.array_equal(host(cb[dev(sample)]), oracle.quantize_codebook(xs))
+    del cb, x
     torch.cuda.empty_cache()
