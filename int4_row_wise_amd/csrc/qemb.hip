@@ -1730,40 +1730,57 @@ __global__ __launch_bounds__(kBlock) void quantize_codebook_kernel(
 }
 
 // Dequantize codebook rows: groups of 16 lanes per row, lane k holding level
-// k; element codes are resolved by ds_bpermute from the group's lanes.  Every
-// lane of a wave runs the same number of passes (rows past the end are
-// clamped and not stored), so the cross-lane reads see all lanes active.
+// k; lane k decodes elements [EPL k, EPL k + EPL) of each pass of 16 EPL
+// elements (EPL = 4 for d <= 64, else 8), each by one ds_bpermute from the
+// lane that holds its level (the pre-masked nibble addresses of the codebook
+// lookup).  Every lane of a wave runs the same number of passes (rows past
+// the end are clamped and not stored), so the cross-lane reads see all lanes
+// active.
+template <int EPL>
 __global__ __launch_bounds__(kBlock) void dequant_codebook_kernel(
     const uint8_t* __restrict__ packed, int64_t rows, int dim, int S, float* __restrict__ y) {
   const int lane = threadIdx.x % kWave;
-  const int k = lane % kCbLevels, gbase = lane - k;
+  const int k = lane % kCbLevels, grp = lane / kCbLevels;
+  const uint32_t gsel = (uint32_t)(grp * 64) * 0x01010101u;
   const int64_t gpb = kBlock / kCbLevels;  // row groups per block
   const int64_t stride_rows = (int64_t)gridDim.x * gpb;
   const int64_t first = (int64_t)blockIdx.x * gpb + threadIdx.x / kCbLevels;
   const int64_t nrounds = (rows + stride_rows - 1) / stride_rows;
-  const int npass = (dim + 127) / 128;  // 16 lanes x 8 elements per pass
+  constexpr int PASS = 16 * EPL;
+  const int npass = (dim + PASS - 1) / PASS;
+  const bool vec = dim % 4 == 0;
   for (int64_t rd = 0; rd < nrounds; ++rd) {
     const int64_t row = first + rd * stride_rows;
     const bool live = row < rows;
     const uint8_t* prow = packed + (live ? row : 0) * (int64_t)S;
-    const float lv = *reinterpret_cast<const float*>(prow + 4 * k);
+    const uint32_t lvb = *reinterpret_cast<const uint32_t*>(prow + 4 * k);
     for (int pss = 0; pss < npass; ++pss) {
-      const int e0 = pss * 128 + 8 * k;
-      const uint32_t cwd = e0 < dim ? *reinterpret_cast<const uint32_t*>(prow + 64 + e0 / 2) : 0u;
-      float o[8];
+      const int e0 = pss * PASS + EPL * k;
+      uint32_t cw = 0u;
+      if (e0 < dim) {
+        if constexpr (EPL == 8) {
+          cw = *reinterpret_cast<const uint32_t*>(prow + 64 + e0 / 2);
+        } else {
+          cw = *reinterpret_cast<const uint16_t*>(prow + 64 + e0 / 2);
+        }
+      }
+      const uint32_t ev = ((cw << 2) & 0x3C3C3C3Cu) | gsel;  // elements 0, 2, ...
+      const uint32_t od = ((cw >> 2) & 0x3C3C3C3Cu) | gsel;  // elements 1, 3, ...
+      float o[EPL];
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        o[j] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
-                                             (gbase + (int)((cwd >> (4 * j)) & 15u)) * 4,
-                                             __builtin_bit_cast(int, lv)));
+      for (int h = 0; h < EPL / 2; ++h) {
+        o[2 * h] = __builtin_bit_cast(float, bperm((int)(ev >> (8 * h)), lvb));
+        o[2 * h + 1] = __builtin_bit_cast(float, bperm((int)(od >> (8 * h)), lvb));
+      }
       if (live && e0 < dim) {
         float* yr = y + row * dim + e0;
-        if (e0 + 8 <= dim && (dim % 4) == 0) {
-          *reinterpret_cast<float4*>(yr) = make_float4(o[0], o[1], o[2], o[3]);
-          *reinterpret_cast<float4*>(yr + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        if (e0 + EPL <= dim && vec) {
+#pragma unroll
+          for (int j = 0; j < EPL; j += 4)
+            *reinterpret_cast<float4*>(yr + j) = make_float4(o[j], o[j + 1], o[j + 2], o[j + 3]);
         } else {
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
+          for (int j = 0; j < EPL; ++j)
             if (e0 + j < dim) yr[j] = o[j];
         }
       }
@@ -2766,9 +2783,13 @@ int qemb_dequantize_codebook(const uint8_t* packed, int64_t rows, int32_t dim, f
   if (!packed || !y) return QEMB_E_INVALID_ARG;
   if (!aligned16(packed) || !aligned16(y)) return QEMB_E_MISALIGNED;
   constexpr int kRowsPerBlock = kBlock / kCbLevels;
-  hipLaunchKernelGGL(dequant_codebook_kernel, dim3(grid_for(rows, kRowsPerBlock, kGridCap)),
-                     dim3(kBlock), 0, reinterpret_cast<hipStream_t>(stream), packed, rows, dim,
-                     (int)qemb_codebook_row_stride(dim), y);
+  const dim3 grid(grid_for(rows, kRowsPerBlock, kGridCap));
+  const int S = (int)qemb_codebook_row_stride(dim);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (dim <= 64)
+    hipLaunchKernelGGL(dequant_codebook_kernel<4>, grid, dim3(kBlock), 0, st, packed, rows, dim, S, y);
+  else
+    hipLaunchKernelGGL(dequant_codebook_kernel<8>, grid, dim3(kBlock), 0, st, packed, rows, dim, S, y);
   return launched();
 }
 
