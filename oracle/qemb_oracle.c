@@ -15,7 +15,9 @@
  *  - Scale and bias stored as binary16 (same page, "Proposed method": fp16
  *    storage of scale and bias; "Main findings": 13.28% of fp32 size at d=128).
  *  - Two 4-bit codes packed per byte (DQRM repository page, paragraph on the
- *    Android demo: INT4 vectors must be bit-packed into INT8 storage).
+ *    Android demo: INT4 vectors must be bit-packed into INT8 storage); 2-bit
+ *    codes (one of the baselines' widths) four per byte, element i at bits
+ *    2 (i mod 4) of byte i / 4.
  *  - Pooled embedding-bag lookup of sparse categorical ids ("Deep Learning
  *    Recommendation Model for Personalization and Recommendation Systems",
  *    review page, "Proposed method": embedding tables map sparse inputs to
@@ -138,7 +140,7 @@ static int64_t code_bytes(int dim, int bits) {
 
 /* Row stride: codes, fp16 scale, fp16 bias, zero padding to 16 bytes. */
 int64_t oracle_row_stride(int dim, int bits) {
-  if (dim < 1 || (bits != 4 && bits != 8)) return -1;
+  if (dim < 1 || (bits != 2 && bits != 4 && bits != 8)) return -1;
   int64_t raw = code_bytes(dim, bits) + 4;
   return (raw + 15) / 16 * 16;
 }
@@ -265,6 +267,14 @@ static void greedy_window(const float* x, int d, int Q, int n_bins, int n_steps,
   *bj = best_j;
 }
 
+/* Code i of a row: 8 / bits codes per byte, element i in bits
+   [bits * (i mod (8 / bits)), ...) of byte i / (8 / bits) -- for 4-bit codes
+   the even element in the low nibble. */
+static void put_code(uint8_t* row, int i, int bits, int q) {
+  int per = 8 / bits;
+  row[i / per] = (uint8_t)(row[i / per] | (q << (bits * (i % per))));
+}
+
 /* Encode one row into its packed form at window [lo, hi]. */
 static void encode_row(const float* x, int d, int bits, float lo, float hi,
                        uint8_t* row, int64_t stride) {
@@ -273,16 +283,7 @@ static void encode_row(const float* x, int d, int bits, float lo, float hi,
   float r = (p.sf == 0.0f) ? 0.0f : 1.0f / p.sf;
   int64_t C = code_bytes(d, bits);
   memset(row, 0, (size_t)stride);
-  for (int i = 0; i < d; ++i) {
-    int q = code_of(x[i], p, r, Q);
-    if (bits == 8) {
-      row[i] = (uint8_t)q;
-    } else if ((i & 1) == 0) {
-      row[i / 2] = (uint8_t)(row[i / 2] | q);         /* even element: low nibble */
-    } else {
-      row[i / 2] = (uint8_t)(row[i / 2] | (q << 4));  /* odd element: high nibble */
-    }
-  }
+  for (int i = 0; i < d; ++i) put_code(row, i, bits, code_of(x[i], p, r, Q));
   row[C + 0] = (uint8_t)(p.s16 & 0xff);
   row[C + 1] = (uint8_t)(p.s16 >> 8);
   row[C + 2] = (uint8_t)(p.b16 & 0xff);
@@ -291,9 +292,8 @@ static void encode_row(const float* x, int d, int bits, float lo, float hi,
 
 /* Read back code i and the parameters of a packed row. */
 static int row_code(const uint8_t* row, int i, int bits) {
-  if (bits == 8) return row[i];
-  uint8_t byte = row[i / 2];
-  return (i & 1) ? (byte >> 4) : (byte & 0x0f);
+  int per = 8 / bits;
+  return (row[i / per] >> (bits * (i % per))) & ((1 << bits) - 1);
 }
 
 static void row_params(const uint8_t* row, int d, int bits, float* sf, float* bf) {
@@ -346,7 +346,7 @@ void oracle_f16_to_f32(const uint16_t* in, float* out, int64_t n) {
 int oracle_quantize_rowwise(const float* x, int64_t rows, int dim, int bits,
                             int clip_mode, int n_bins, int n_steps,
                             uint8_t* packed, int32_t* best_ij) {
-  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 2 && bits != 4 && bits != 8)) return OR_INVALID;
   if (clip_mode != 0 && clip_mode != 1) return OR_INVALID;
   if (clip_mode == 1 && (n_bins < 1 || n_steps < 0 || n_steps >= n_bins)) return OR_INVALID;
   int64_t stride = oracle_row_stride(dim, bits);
@@ -472,14 +472,7 @@ static void encode_symmetric(const float* x, int d, int bits, uint8_t* row, int6
     float q = sf == 0.0f ? 0.0f : rintf(x[i] * r);
     if (q < -(float)Qs) q = -(float)Qs;
     if (q > (float)Qs) q = (float)Qs;
-    int c = (int)q + H;
-    if (bits == 8) {
-      row[i] = (uint8_t)c;
-    } else if ((i & 1) == 0) {
-      row[i / 2] = (uint8_t)(row[i / 2] | c);
-    } else {
-      row[i / 2] = (uint8_t)(row[i / 2] | (c << 4));
-    }
+    put_code(row, i, bits, (int)q + H);
   }
   row[C + 0] = (uint8_t)(s16 & 0xff);
   row[C + 1] = (uint8_t)(s16 >> 8);
@@ -490,7 +483,7 @@ static void encode_symmetric(const float* x, int d, int bits, uint8_t* row, int6
 /* The window a baseline picks for one row (symmetric: [-max|x|, max|x|]). */
 int oracle_baseline_window(const float* x, int dim, int bits, int method, float param,
                            float* lo_hi) {
-  if (dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  if (dim < 1 || dim > OR_MAX_DIM || (bits != 2 && bits != 4 && bits != 8)) return OR_INVALID;
   float lo, hi;
   if (method == OR_BASE_SYMMETRIC) {
     float m = 0.0f;
@@ -514,7 +507,7 @@ int oracle_baseline_window(const float* x, int dim, int bits, int method, float 
    OR_BASE_ACIQ; rows in the packed format of oracle_quantize_rowwise. */
 int oracle_quantize_baseline(const float* x, int64_t rows, int dim, int bits, int method,
                              float param, uint8_t* packed) {
-  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 2 && bits != 4 && bits != 8)) return OR_INVALID;
   if (method < OR_BASE_SYMMETRIC || method > OR_BASE_ACIQ) return OR_INVALID;
   if (method == OR_BASE_PERCENTILE && !(param >= 0.5f && param <= 1.0f)) return OR_INVALID;
   int64_t stride = oracle_row_stride(dim, bits);
@@ -567,7 +560,7 @@ float oracle_row_sse(const float* x, const uint8_t* row, int dim, int bits) {
 }
 
 int oracle_dequantize(const uint8_t* packed, int64_t rows, int dim, int bits, float* y) {
-  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 4 && bits != 8)) return OR_INVALID;
+  if (rows < 0 || dim < 1 || dim > OR_MAX_DIM || (bits != 2 && bits != 4 && bits != 8)) return OR_INVALID;
   int64_t stride = oracle_row_stride(dim, bits);
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r) {
@@ -770,7 +763,7 @@ int oracle_bag_forward(const uint8_t* packed, int64_t total_rows,
                        int64_t nnz, int index_type, int pool_mode,
                        const float* weights, double* out, double* abs_terms,
                        int64_t* err_count) {
-  if (bits != 4 && bits != 8) return OR_INVALID;
+  if (bits != 2 && bits != 4 && bits != 8) return OR_INVALID;
   return bag_forward_fmt(packed, total_rows, table_offsets, T, B, dim, bits, indices, offsets,
                          nnz, index_type, pool_mode, weights, out, abs_terms, err_count);
 }
@@ -840,7 +833,7 @@ static int l2_error_fmt(const float* x, const uint8_t* packed, int64_t rows, int
 
 int oracle_l2_error(const float* x, const uint8_t* packed, int64_t rows, int dim,
                     int bits, double* out4) {
-  if (bits != 4 && bits != 8) return OR_INVALID;
+  if (bits != 2 && bits != 4 && bits != 8) return OR_INVALID;
   return l2_error_fmt(x, packed, rows, dim, bits, out4);
 }
 

@@ -163,19 +163,7 @@ def encode(x, bits, clip="range", n_bins=200, n_steps=100):
         lo, hi, _, _ = greedy(x, bits, n_bins, n_steps)
     s16, b16, sf, bf = params(lo, hi, Q)
     q = codes(x, sf, bf, Q)
-    d = x.size
-    C = (d * bits + 7) // 8
-    S = (C + 4 + 15) // 16 * 16
-    row = np.zeros(S, dtype=np.uint8)
-    if bits == 8:
-        row[:d] = q
-    else:
-        qq = np.zeros(2 * C, dtype=np.int64)
-        qq[:d] = q
-        row[:C] = (qq[0::2] | (qq[1::2] << 4)).astype(np.uint8)
-    row[C:C + 2] = [s16 & 0xFF, s16 >> 8]
-    row[C + 2:C + 4] = [b16 & 0xFF, b16 >> 8]
-    return row
+    return _pack(q, bits, s16, b16)
 
 
 # ---- codebook rows: 16 levels from 1-D k-means (Lloyd), 4-bit codes ----
@@ -244,16 +232,20 @@ def encode_symmetric(x, bits):
 
 
 def _pack(codes, bits, s16, b16):
+    """Row bytes: codes (8 / bits per byte, element i at bits
+    bits * (i mod per) of byte i // per), fp16 scale and bias little-endian,
+    zero padding to 16 bytes."""
     d = codes.size
     C = (d * bits + 7) // 8
     S = (C + 4 + 15) // 16 * 16
     row = np.zeros(S, dtype=np.uint8)
-    if bits == 8:
-        row[:d] = codes
-    else:
-        qq = np.zeros(2 * C, dtype=np.int64)
-        qq[:d] = codes
-        row[:C] = (qq[0::2] | (qq[1::2] << 4)).astype(np.uint8)
+    per = 8 // bits
+    qq = np.zeros(per * C, dtype=np.int64)
+    qq[:d] = codes
+    acc = np.zeros(C, dtype=np.int64)
+    for j in range(per):
+        acc |= qq[j::per] << (bits * j)
+    row[:C] = acc.astype(np.uint8)
     row[C:C + 2] = [s16 & 0xFF, s16 >> 8]
     row[C + 2:C + 4] = [b16 & 0xFF, b16 >> 8]
     return row

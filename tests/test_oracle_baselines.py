@@ -38,7 +38,7 @@ def _rows(seed, n, d):
     return x
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("dim", [1, 3, 16, 33, 64])
 def test_baselines_match_numpy_model(dim, bits):
     x = _rows(700 + dim + bits, 12, dim)
@@ -100,7 +100,7 @@ def test_aciq_is_range_when_the_ratio_exceeds_the_range():
     assert np.array_equal(oracle.quantize_baseline(x, 8, oracle.ACIQ), oracle.quantize_rowwise(x, 8))
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_symmetric_grid_closed_forms(bits):
     H = 1 << (bits - 1)
     g = np.random.default_rng(5)
@@ -124,7 +124,7 @@ def test_symmetric_grid_closed_forms(bits):
 
 def test_symmetric_scale_cap_keeps_the_bias_finite():
     x = np.array([[65504.0, -3.0, 1.0, 0.5]], np.float32)
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         y = oracle.dequantize(oracle.quantize_baseline(x, bits, oracle.SYMMETRIC), 4, bits)
         assert np.all(np.isfinite(y))
         H = 1 << (bits - 1)

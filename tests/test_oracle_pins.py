@@ -22,6 +22,13 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 def unpack_codes(packed_row: np.ndarray, dim: int, bits: int) -> np.ndarray:
     if bits == 8:
         return packed_row[:dim].astype(np.int64)
+    if bits == 2:
+        C = (dim + 3) // 4
+        b = packed_row[:C].astype(np.int64)
+        q = np.empty(4 * C, dtype=np.int64)
+        for j in range(4):
+            q[j::4] = (b >> (2 * j)) & 3
+        return q[:dim]
     C = (dim + 1) // 2
     b = packed_row[:C].astype(np.int64)
     q = np.empty(2 * C, dtype=np.int64)
@@ -98,7 +105,8 @@ def test_row_bytes_reproduce_printed_size_ratio(oracle_lib):
 
 @pytest.mark.parametrize("dim,bits,stride", [(16, 4, 16), (64, 4, 48), (128, 4, 80), (128, 8, 144),
                                              (1, 4, 16), (12, 8, 16), (13, 8, 32), (24, 4, 16),
-                                             (25, 4, 32)])
+                                             (25, 4, 32), (128, 2, 48), (48, 2, 16), (49, 2, 32),
+                                             (5, 2, 16)])
 def test_row_stride(oracle_lib, dim, bits, stride):
     assert oracle.row_stride(dim, bits) == stride
 
@@ -131,7 +139,7 @@ def _grid_rows(g, n, dim, bits):
     return np.stack(rows), np.stack(ks), ss, bs
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("dim", [2, 7, 16, 64])
 def test_grid_rows_round_trip_exactly(oracle_lib, bits, dim):
     g = np.random.default_rng(100 + dim + bits)
@@ -148,6 +156,11 @@ def test_grid_rows_round_trip_exactly(oracle_lib, bits, dim):
             kk = np.zeros(2 * C, dtype=np.int64)
             kk[:dim] = k[r]
             assert np.array_equal(packed[r, :C], (kk[0::2] | (kk[1::2] << 4)).astype(np.uint8))
+        elif bits == 2:
+            kk = np.zeros(4 * C, dtype=np.int64)
+            kk[:dim] = k[r]
+            assert np.array_equal(packed[r, :C], (kk[0::4] | (kk[1::4] << 2) | (kk[2::4] << 4) |
+                                                  (kk[3::4] << 6)).astype(np.uint8))
         else:
             assert np.array_equal(packed[r, :C], k[r].astype(np.uint8))
     y = oracle.dequantize(packed, dim, bits)
@@ -179,7 +192,7 @@ def _ulp32(v):
     return (np.nextafter(v, np.float32(np.inf)) - v).astype(np.float64)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("dim", [3, 16, 64, 128])
 def test_range_error_bound_and_nearest_code(oracle_lib, bits, dim):
     """Each element lands on the grid point nearest to it (brute force over all
@@ -271,7 +284,7 @@ def test_l2_error_against_numpy(oracle_lib):
 # greedy search
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_greedy_with_zero_steps_is_range_encoding(oracle_lib, bits):
     g = np.random.default_rng(21)
     x = (g.standard_normal((300, 33)) * 0.02).astype(np.float32)
@@ -285,7 +298,7 @@ def _sse64(x, packed, dim, bits):
     return ((x.astype(np.float64) - y) ** 2).sum(axis=1)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("dim", [16, 64])
 def test_greedy_never_worse_than_range(oracle_lib, bits, dim):
     g = np.random.default_rng(31 + dim)
@@ -365,7 +378,7 @@ def test_oracle_matches_independent_numpy_model_bit_for_bit(oracle_lib):
     g = np.random.default_rng(61)
     n_cases = 0
     for d in (1, 2, 3, 4, 5, 8, 16):
-        for bits in (4, 8):
+        for bits in (2, 4, 8):
             for _ in range(12):
                 scale = float(g.choice([1e-3, 0.02, 1.0, 300.0]))
                 x = (g.standard_normal(d) * scale).astype(np.float32)
@@ -382,7 +395,7 @@ def test_oracle_matches_independent_numpy_model_bit_for_bit(oracle_lib):
                     ref = nm.encode(x, bits, clip, Bn, K)
                     assert np.array_equal(ours, ref), (d, bits, clip, Bn, K, x)
                     n_cases += 1
-    assert n_cases == 7 * 2 * 12 * 2
+    assert n_cases == 7 * 3 * 12 * 2
 
 
 def test_oracle_rejects_values_outside_fp16_range(oracle_lib):
@@ -404,7 +417,7 @@ def _table(g, rows, dim, bits):
     return x, oracle.quantize_rowwise(x, bits)
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("weighted", [False, True])
 @pytest.mark.parametrize("itype", [np.int32, np.int64])
 def test_bag_matches_torch_embedding_bag(oracle_lib, bits, weighted, itype):
