@@ -326,10 +326,20 @@ def quantizer_extras(q, synth, torch, dev, reps=3):
                                    "hbm_frac": (in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS,
                                    "l2": q.l2_error(x, pk, 4)}
     del pk
+    # 2-bit rows (range), the narrowest width of the comparison
+    pk2 = torch.empty((rows, q.row_stride(dim, 2)), dtype=torch.uint8, device=dev)
+    out2_b = rows * ((dim * 2 + 7) // 8 + 4)
+    ms = timed(lambda: q.quantize_rowwise(x, 2, q.RANGE, out=pk2), reps)
+    res["int2_range_quantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3,
+                                  "GBps": (in_b + out2_b) / ms / 1e6,
+                                  "hbm_frac": (in_b + out2_b) / ms / 1e6 / HBM_PEAK_GBS,
+                                  "l2": q.l2_error(x, pk2, 2)}
+    del pk2
     res["l2_mean_row_by_method"] = {
         k: res[k]["mean_row"] for k in ("codebook_l2", "greedy_l2", "range_l2")} | {
         "baseline_" + n + "_l2": res["baseline_" + n]["l2"]["mean_row"]
-        for n in ("symmetric", "percentile_0.99", "aciq")}
+        for n in ("symmetric", "percentile_0.99", "aciq")} | {
+        "int2_range_l2": res["int2_range_quantize"]["l2"]["mean_row"]}
     cb_out = rows * cb.shape[1]
     ms = timed(lambda: q.dequantize_codebook(cb, dim, out=y), reps)
     res["codebook_dequantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3,

@@ -11,7 +11,8 @@
  *    row's squared error ("Post-Training 4-bit Quantization on Embedding
  *    Tables", review page, sections "Proposed method" and "Main findings").
  *  - 4-bit codes are bit-packed two per byte (DQRM repository page, the
- *    paragraph on the Android demo).
+ *    paragraph on the Android demo); 2-bit codes, one of the widths the
+ *    quantizer comparison uses, four per byte.
  *  - Pooled lookup: sparse categorical ids select rows of many embedding
  *    tables and each bag of ids is reduced to one dense vector ("Deep
  *    Learning Recommendation Model for Personalization and Recommendation
@@ -23,7 +24,8 @@
  * C = ceil(dim * bits / 8)):
  *     bytes [0, C)      codes; INT4: element 2k in the low nibble of byte k,
  *                       element 2k+1 in the high nibble (0 for odd dim);
- *                       INT8: element k in byte k
+ *                       INT8: element k in byte k; INT2: element 4k+j in
+ *                       bits [2j, 2j+2) of byte k
  *     bytes [C, C+2)    scale, binary16, little-endian
  *     bytes [C+2, C+4)  bias,  binary16, little-endian
  *     bytes [C+4, S)    zero
@@ -104,7 +106,7 @@ int qemb_abi_version(void);
 const char* qemb_strerror(int code);
 
 /* Packed row stride S in bytes for (dim, bits), or -1 if dim < 1,
- * dim > QEMB_MAX_DIM or bits is not 4 or 8. */
+ * dim > QEMB_MAX_DIM or bits is not 2, 4 or 8. */
 int64_t qemb_row_stride(int32_t dim, int32_t bits);
 
 /*
@@ -115,7 +117,8 @@ int64_t qemb_row_stride(int32_t dim, int32_t bits);
  *   x       [rows][dim] fp32, row-major, 16-byte aligned
  *   rows    >= 0 (0 = nothing to do)
  *   dim     1 .. QEMB_MAX_DIM
- *   bits    4 or 8
+ *   bits    2, 4 or 8 (every other entry point taking `bits` accepts the
+ *           same three widths)
  *   clip_mode  QEMB_CLIP_RANGE or QEMB_CLIP_GREEDY
  *   n_bins, n_steps  greedy only: 1 <= n_bins, 0 <= n_steps < n_bins
  *                    (ignored for range mode)

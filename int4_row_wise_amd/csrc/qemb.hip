@@ -396,7 +396,13 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(const uint8_t* __restri
       const int e0 = (c * LPR + s) * EPL;
       if (e0 >= dim) break;
       float o[EPL];
-      if (BITS == 4) {
+      if (BITS == 2) {
+        // 8 two-bit codes in 2 bytes; a code under a binary16 zero exponent
+        // reads as code * 2^-24, as in decode_dword
+        const uint32_t wd = *reinterpret_cast<const uint16_t*>(prow + e0 / 4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k] = __builtin_fmaf(sfs, h16((wd >> (2 * k)) & 3u), bf);
+      } else if (BITS == 4) {
         float yk[8];
         decode_dword<4>(*reinterpret_cast<const uint32_t*>(prow + e0 / 2), sfs, bf, yk);
 #pragma unroll
@@ -1367,7 +1373,9 @@ __global__ __launch_bounds__(kBlock) void l2_partial_kernel(const float* __restr
     const float sf = half_value(p), bf = half_value(p >> 16);
     double e2 = 0.0, x2 = 0.0;
     for (int k = 0; k < dim; ++k) {
-      uint32_t q = bits == 8 ? prow[k] : ((prow[k >> 1] >> ((k & 1) * 4)) & 15u);
+      uint32_t q = bits == 8   ? prow[k]
+                   : bits == 4 ? ((prow[k >> 1] >> ((k & 1) * 4)) & 15u)
+                               : ((prow[k >> 2] >> ((k & 3) * 2)) & 3u);
       const double yk = (double)__builtin_fmaf(sf, (float)q, bf);
       const double xk = (double)xr[k];
       const double e = xk - yk;
@@ -1424,11 +1432,12 @@ __global__ __launch_bounds__(kBlock) void l2_final_kernel(const double* __restri
 // ---------------------------------------------------------------------------
 
 constexpr int kBaseSym = 0, kBasePct = 1, kBaseAciq = 2;
+constexpr int kBaseRange = 3;  // the row range: the range rule's window (used for 2-bit rows)
 
-// W(3 4^b) as binary32: 5.0286403 (b = 4), 9.8967600 (b = 8)
+// W(3 4^b) as binary32: 2.8306830 (b = 2), 5.0286403 (b = 4), 9.8967600 (b = 8)
 template <int BITS>
 __device__ __forceinline__ float aciq_ratio() {
-  return __builtin_bit_cast(float, BITS == 4 ? 0x40a0ea9fu : 0x411e5921u);
+  return __builtin_bit_cast(float, BITS == 2 ? 0x403529e9u : BITS == 4 ? 0x40a0ea9fu : 0x411e5921u);
 }
 
 template <int EPL, int LPR>
@@ -1511,7 +1520,10 @@ __global__ __launch_bounds__(kBlock) void quantize_baseline_kernel(
       }
       mn = group_min<LPR>(mn) + 0.0f;
       mx = group_max<LPR>(mx) + 0.0f;
-      if constexpr (METHOD == kBaseAciq) {
+      if constexpr (METHOD == kBaseRange) {
+        lo = mn;
+        hi = mx;
+      } else if constexpr (METHOD == kBaseAciq) {
         float u[EPL];
 #pragma unroll
         for (int k = 0; k < EPL; ++k) u[k] = k < valid ? v[k] : 0.0f;
@@ -1916,6 +1928,123 @@ __global__ __launch_bounds__(kBlock) void bag_codebook_kernel(
     body(std::false_type{});
   }
   // the 4 groups' partial sums: lanes i, i^32, i^16, i^48
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float x0 = acc[pp][j], x1 = acc[pp][j];
+      permlane32_swap(x0, x1);
+      const float h = x0 + x1;
+      float y0 = h, y1 = h;
+      permlane16_swap(y0, y1);
+      acc[pp][j] = y0 + y1;
+    }
+  if (grp == 0) {
+    float* o = out + (b * T + t) * (int64_t)dim;
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp) {
+      const int e0 = pp * 128 + 8 * k;
+      if (e0 + 8 <= dim && (dim % 4) == 0) {
+        *reinterpret_cast<float4*>(o + e0) = make_float4(acc[pp][0], acc[pp][1], acc[pp][2], acc[pp][3]);
+        *reinterpret_cast<float4*>(o + e0 + 4) = make_float4(acc[pp][4], acc[pp][5], acc[pp][6], acc[pp][7]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (e0 + j < dim) o[e0 + j] = acc[pp][j];
+      }
+    }
+  }
+  for (int m = 1; m < kWave; m <<= 1) errs += __shfl_xor(errs, m);
+  if (lane == 0 && errs && err_count) atomicAdd(err_count, errs);
+}
+
+// Pooled lookup over 2-bit rows: the mapping of bag_codebook_kernel (one
+// wave per bag, 4 groups of 16 lanes, owner-lane ids, buffer-descriptor
+// rows), lane k of a group decoding elements [8k, 8k + 8) of each
+// 128-element pass from 2 code bytes; the term is w * fmaf(sf, q, bf) (the
+// decoded value times the weight, as the other uniform-row lookups).
+template <typename IdxT, int NP, int U>
+__global__ __launch_bounds__(kBlock) void bag_int2_kernel(
+    const uint8_t* __restrict__ packed, int64_t S, int64_t total_rows,
+    const int64_t* __restrict__ table_offsets, int T, int64_t B, int dim, int C,
+    const void* __restrict__ indices, const void* __restrict__ offsets, int64_t nnz,
+    const float* __restrict__ weights, float* __restrict__ out, int32_t* __restrict__ err_count,
+    int64_t n_bags) {
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int k = lane % 16, grp = lane / 16;
+  const int64_t bag = (int64_t)blockIdx.x * kWPB + wv;
+  if (bag >= n_bags) return;
+  const int64_t t = bag / B, b = bag - t * B;
+  int errs = 0;
+  int64_t p0 = load_index<IdxT>(offsets, bag), p1 = load_index<IdxT>(offsets, bag + 1);
+  if (!uniform_flag(p0 >= 0 && p1 >= p0 && p1 <= nnz)) {
+    errs = lane == 0 ? 1 : 0;
+    p0 = p1 = 0;
+  }
+  const int64_t a0 = table_offsets[t], a1 = table_offsets[t + 1];
+  const bool tab_ok = uniform_flag(a0 >= 0 && a1 > a0 && a1 <= total_rows);
+  const int64_t nt = tab_ok ? a1 - a0 : 0;
+  const uint8_t* base = packed + (tab_ok ? a0 : 0) * S;
+  const IdxT* ids = reinterpret_cast<const IdxT*>(indices);
+  if (total_rows == 0) {
+    errs += lane == 0 ? (int)(p1 - p0) : 0;
+    p1 = p0;
+  }
+  const int c4 = C & ~3, c4n = c4 + 4 < (int)S ? c4 + 4 : (int)S - 4;
+  const uint32_t csh = (uint32_t)(C & 3);
+  float acc[NP][8];
+#pragma unroll
+  for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[pp][j] = 0.0f;
+  for (int64_t c = p0; c < p1; c += kWave) {
+    const int n = (int)min<int64_t>(kWave, p1 - c);
+    const bool in = lane < n;
+    const int64_t id = in ? (int64_t)ids[c + lane] : 0;
+    const bool ok = in && id >= 0 && id < nt;
+    errs += (in && !ok) ? 1 : 0;
+    const int64_t off = (ok ? id : 0) * S;  // absent: row 0, weight 0
+    const uint32_t own_lo = (uint32_t)off, own_hi = (uint32_t)(off >> 32);
+    const int wt = __builtin_bit_cast(int, ok ? (weights ? weights[c + lane] : 1.0f) : 0.0f);
+    const int nr = (n + 3) / 4;
+    for (int r0 = 0; r0 < nr; r0 += U) {
+      float wl[U], sf[U], bf[U];
+      uint32_t cwd[U][NP];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (r0 + u < nr) {
+          const int src = 16 * (r0 + u) + 4 * grp;
+          wl[u] = __builtin_bit_cast(float, (int)bperm(src, (uint32_t)wt));
+          const uint64_t hi = bperm(src, own_hi);
+          const uint8_t* prow = base + ((hi << 32) | bperm(src, own_lo));
+          const uint32_t plo = *reinterpret_cast<const uint32_t*>(prow + c4);
+          const uint32_t phi = *reinterpret_cast<const uint32_t*>(prow + c4n);
+          const uint32_t p32 = __builtin_amdgcn_alignbyte(phi, plo, csh);
+          sf[u] = half_value(p32);
+          bf[u] = half_value(p32 >> 16);
+#pragma unroll
+          for (int pp = 0; pp < NP; ++pp) {
+            const int e0 = pp * 128 + 8 * k;
+            cwd[u][pp] = e0 < dim ? *reinterpret_cast<const uint16_t*>(prow + e0 / 4) : 0u;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (r0 + u < nr) {
+#pragma unroll
+          for (int pp = 0; pp < NP; ++pp) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float y = __builtin_fmaf(sf[u], (float)((cwd[u][pp] >> (2 * j)) & 3u), bf[u]);
+              acc[pp][j] = __builtin_fmaf(wl[u], y, acc[pp][j]);
+            }
+          }
+        }
+      }
+    }
+  }
 #pragma unroll
   for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
@@ -2535,6 +2664,31 @@ int dispatch_wave(const BagArgs& a, hipStream_t st) {
 // C ABI
 // ---------------------------------------------------------------------------
 
+int dispatch_bag_int2(const BagArgs& a, hipStream_t st) {
+  const int64_t blocks = (a.n_bags + kWPB - 1) / kWPB;
+  if (blocks > 0x7fffffff) return QEMB_E_UNSUPPORTED;
+  const int np = (a.dim + 127) / 128;
+  auto go = [&](auto idx_tag, auto np_tag) {
+    using IdxT = decltype(idx_tag);
+    constexpr int NP = decltype(np_tag)::value;
+    constexpr int U = NP <= 2 ? 8 : NP == 4 ? 4 : 2;
+    hipLaunchKernelGGL((bag_int2_kernel<IdxT, NP, U>), dim3((unsigned)blocks), dim3(kBlock), 0, st,
+                       a.packed, a.S, a.total_rows, a.table_offsets, a.T, a.B, a.dim, a.C, a.indices,
+                       a.offsets, a.nnz, a.weights, a.out, a.err_count, a.n_bags);
+    return launched();
+  };
+  auto by_np = [&](auto idx_tag) {
+    switch (np) {
+      case 1: return go(idx_tag, std::integral_constant<int, 1>{});
+      case 2: return go(idx_tag, std::integral_constant<int, 2>{});
+      case 3:
+      case 4: return go(idx_tag, std::integral_constant<int, 4>{});
+      default: return go(idx_tag, std::integral_constant<int, 8>{});
+    }
+  };
+  return a.idx64 ? by_np(int64_t{}) : by_np(int32_t{});
+}
+
 template <int BITS, int EPL, int LPR, int METHOD>
 int launch_baseline(const float* x, int64_t rows, int dim, int C, int S, int vec4, float param,
                     uint8_t* packed, hipStream_t st) {
@@ -2648,14 +2802,14 @@ const char* qemb_strerror(int code) {
 }
 
 int64_t qemb_row_stride(int32_t dim, int32_t bits) {
-  if (dim < 1 || dim > QEMB_MAX_DIM || (bits != 4 && bits != 8)) return -1;
+  if (dim < 1 || dim > QEMB_MAX_DIM || (bits != 2 && bits != 4 && bits != 8)) return -1;
   return (code_bytes(dim, bits) + 4 + 15) / 16 * 16;
 }
 
 int qemb_quantize_rowwise(const float* x, int64_t rows, int32_t dim, int32_t bits,
                           int32_t clip_mode, int32_t n_bins, int32_t n_steps, uint8_t* packed,
                           qemb_stream_t stream) {
-  if (rows < 0 || dim < 1 || (bits != 4 && bits != 8)) return QEMB_E_INVALID_ARG;
+  if (rows < 0 || dim < 1 || (bits != 2 && bits != 4 && bits != 8)) return QEMB_E_INVALID_ARG;
   if (clip_mode != QEMB_CLIP_RANGE && clip_mode != QEMB_CLIP_GREEDY) return QEMB_E_INVALID_ARG;
   if (clip_mode == QEMB_CLIP_GREEDY && (n_bins < 1 || n_steps < 0 || n_steps >= n_bins))
     return QEMB_E_INVALID_ARG;
@@ -2668,16 +2822,18 @@ int qemb_quantize_rowwise(const float* x, int64_t rows, int32_t dim, int32_t bit
   const int vec4 = (dim % 4 == 0);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (clip_mode == QEMB_CLIP_RANGE) {
+    if (bits == 2) return baseline_by_dim<2, kBaseRange>(x, rows, dim, C, S, vec4, 0.0f, packed, st);
     return bits == 4 ? dispatch_range<4>(x, rows, dim, C, S, vec4, packed, st)
                      : dispatch_range<8>(x, rows, dim, C, S, vec4, packed, st);
   }
+  if (bits == 2) return dispatch_greedy<2>(x, rows, dim, C, S, vec4, n_bins, n_steps, packed, st);
   return bits == 4 ? dispatch_greedy<4>(x, rows, dim, C, S, vec4, n_bins, n_steps, packed, st)
                    : dispatch_greedy<8>(x, rows, dim, C, S, vec4, n_bins, n_steps, packed, st);
 }
 
 int qemb_dequantize(const uint8_t* packed, int64_t rows, int32_t dim, int32_t bits, float* y,
                     qemb_stream_t stream) {
-  if (rows < 0 || dim < 1 || (bits != 4 && bits != 8)) return QEMB_E_INVALID_ARG;
+  if (rows < 0 || dim < 1 || (bits != 2 && bits != 4 && bits != 8)) return QEMB_E_INVALID_ARG;
   if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
   if (rows == 0) return QEMB_OK;
   if (!packed || !y) return QEMB_E_INVALID_ARG;
@@ -2686,6 +2842,7 @@ int qemb_dequantize(const uint8_t* packed, int64_t rows, int32_t dim, int32_t bi
   const int S = (int)qemb_row_stride(dim, bits);
   const int vec4 = (dim % 4 == 0);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (bits == 2) return dispatch_dequant<2>(packed, rows, dim, C, S, vec4, y, st);
   return bits == 4 ? dispatch_dequant<4>(packed, rows, dim, C, S, vec4, y, st)
                    : dispatch_dequant<8>(packed, rows, dim, C, S, vec4, y, st);
 }
@@ -2695,7 +2852,7 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
                      const void* offsets, int64_t nnz, int32_t index_type, int32_t pool_mode,
                      const float* weights, float* out, int32_t* err_count,
                      qemb_stream_t stream) {
-  if (T < 0 || B < 0 || dim < 1 || (bits != 4 && bits != 8) || total_rows < 0 || nnz < 0)
+  if (T < 0 || B < 0 || dim < 1 || (bits != 2 && bits != 4 && bits != 8) || total_rows < 0 || nnz < 0)
     return QEMB_E_INVALID_ARG;
   if (index_type != QEMB_INDEX_INT32 && index_type != QEMB_INDEX_INT64) return QEMB_E_INVALID_ARG;
   if (pool_mode != QEMB_POOL_SUM && pool_mode != QEMB_POOL_WEIGHTED_SUM) return QEMB_E_INVALID_ARG;
@@ -2726,6 +2883,7 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
   a.n_bags = (int64_t)T * B;
   a.vec4 = (dim % 4 == 0);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (bits == 2) return dispatch_bag_int2(a, st);
   // multi-hot bags (8+ ids on average): one wave per bag
   const int64_t mean_len = (nnz + a.n_bags - 1) / a.n_bags;
   if (mean_len >= 8) return bits == 4 ? dispatch_wave<4>(a, st) : dispatch_wave<8>(a, st);
@@ -2744,7 +2902,7 @@ size_t qemb_l2_error_workspace_bytes(void) { return (size_t)kL2Blocks * 4 * size
 
 int qemb_quantize_baseline(const float* x, int64_t rows, int32_t dim, int32_t bits, int32_t method,
                            float param, uint8_t* packed, qemb_stream_t stream) {
-  if (rows < 0 || dim < 1 || (bits != 4 && bits != 8)) return QEMB_E_INVALID_ARG;
+  if (rows < 0 || dim < 1 || (bits != 2 && bits != 4 && bits != 8)) return QEMB_E_INVALID_ARG;
   if (method != QEMB_BASE_SYMMETRIC && method != QEMB_BASE_PERCENTILE && method != QEMB_BASE_ACIQ)
     return QEMB_E_INVALID_ARG;
   if (method == QEMB_BASE_PERCENTILE && !(param >= 0.5f && param <= 1.0f)) return QEMB_E_INVALID_ARG;
@@ -2755,6 +2913,7 @@ int qemb_quantize_baseline(const float* x, int64_t rows, int32_t dim, int32_t bi
   const int C = (int)code_bytes(dim, bits), S = (int)qemb_row_stride(dim, bits);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int vec4 = dim % 4 == 0;
+  if (bits == 2) return baseline_by_method<2>(method, x, rows, dim, C, S, vec4, param, packed, st);
   return bits == 4 ? baseline_by_method<4>(method, x, rows, dim, C, S, vec4, param, packed, st)
                    : baseline_by_method<8>(method, x, rows, dim, C, S, vec4, param, packed, st);
 }
@@ -2886,7 +3045,7 @@ int qemb_l2_error_codebook(const float* x, const uint8_t* packed, int64_t rows, 
 
 int qemb_l2_error(const float* x, const uint8_t* packed, int64_t rows, int32_t dim, int32_t bits,
                   void* workspace, double* out4, qemb_stream_t stream) {
-  if (rows < 0 || dim < 1 || (bits != 4 && bits != 8)) return QEMB_E_INVALID_ARG;
+  if (rows < 0 || dim < 1 || (bits != 2 && bits != 4 && bits != 8)) return QEMB_E_INVALID_ARG;
   if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
   if (!workspace || !out4 || (rows > 0 && (!x || !packed))) return QEMB_E_INVALID_ARG;
   if ((x && !aligned16(x)) || (packed && !aligned16(packed)) || !aligned16(workspace))

@@ -45,12 +45,12 @@ def test_abi_version_and_strerror(lib):
 
 
 def test_row_stride_matches_oracle(lib):
-    for bits in (4, 8):
+    for bits in (2, 4, 8):
         for dim in range(1, 1025):
             assert lib.qemb_row_stride(dim, bits) == oracle.row_stride(dim, bits)
     assert lib.qemb_row_stride(0, 4) == -1
     assert lib.qemb_row_stride(1025, 4) == -1
-    assert lib.qemb_row_stride(16, 5) == -1
+    assert lib.qemb_row_stride(16, 5) == -1 and lib.qemb_row_stride(16, 3) == -1
 
 
 FAKE = ctypes.c_void_p(1 << 20)       # never dereferenced: validation fails first
@@ -173,6 +173,7 @@ def test_baseline_argument_errors(lib):
     #        x     rows dim bits meth param packed stream
     assert f(FAKE, -1, 16, 4, 0, 0.0, FAKE, None) == -1
     assert f(FAKE, 10, 16, 5, 0, 0.0, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 3, 0, 0.0, FAKE, None) == -1
     assert f(FAKE, 10, 16, 4, 3, 0.0, FAKE, None) == -1
     assert f(FAKE, 10, 16, 4, 1, 0.4, FAKE, None) == -1
     assert f(FAKE, 10, 16, 4, 1, 1.5, FAKE, None) == -1
