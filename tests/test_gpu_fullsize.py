@@ -274,3 +274,43 @@ def test_baselines_quantizer_workload_full(q):
     assert np.array_equal(host(cb[dev(sample)]), oracle.quantize_codebook(xs))
     del cb, x
     torch.cuda.empty_cache()
+
+
+def test_tables_over_2gb_take_64bit_addressing(q):
+    """A table of more than 2 GB of packed rows (28M rows of d=128: 2.24 GB
+    INT4, 4.0 GB INT8, 3.6 GB codebook) beside a small one: the lookups read
+    rows of such a table with 64-bit addresses instead of a buffer
+    descriptor.  Sampled bags against the oracle, counts exact."""
+    import torch
+    w = synth.scaled(synth.workload(4), rows=(28_000_000, 1000), batch=2000)
+    print("tables over 2 GB", flush=True)
+    bt = synth.batch(w, batch_seed=0, index_dtype=np.int32)
+    toff = dev(bt.table_offsets)
+    far = int(np.sum(bt.indices[: bt.offsets[bt.B]] >= (1 << 31) // 80))
+    assert far > 100  # ids past the first 2 GB of the INT4 table
+    for bits in (4, 8):
+        packed = pack_tables(q, w, bits, q.RANGE)
+        assert packed.shape[1] * w.rows[0] > (1 << 31)
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        out = host(q.bag_forward(packed, toff, bt.B, w.dim, bits, dev(bt.indices), dev(bt.offsets),
+                                 dev(bt.weights), err_count=err))
+        assert int(host(err)[0]) == 0
+        check_sampled_bags(q, w, packed, bits, oracle.RANGE, bt, out, 300, 95 + bits)
+        del packed
+    S = q.codebook_row_stride(w.dim)
+    cb = torch.empty((w.total_rows, S), dtype=torch.uint8, device="cuda")
+    r0 = 0
+    for t in range(w.n_tables):
+        for c0 in range(0, w.rows[t], 1 << 24):
+            m = min(1 << 24, w.rows[t] - c0)
+            x = synth.table_values_torch(w, t, c0, m, "cuda")
+            q.quantize_codebook(x, out=cb[r0 + c0:r0 + c0 + m])
+            del x
+        r0 += w.rows[t]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = host(q.bag_forward_codebook(cb, toff, bt.B, w.dim, dev(bt.indices), dev(bt.offsets),
+                                      dev(bt.weights), err_count=err))
+    assert int(host(err)[0]) == 0
+    check_sampled_bags(q, w, cb, 4, None, bt, out, 300, 99, codebook=True)
+    del cb
+    torch.cuda.empty_cache()
