@@ -541,6 +541,15 @@ def main():
             "launch_ms": launch_stats(msc), "GBps": b0 / (np.median(msc) * 1e-3) / 1e9,
             "hbm_frac": b0 / (np.median(msc) * 1e-3) / 1e9 / HBM_PEAK_GBS}
         result["interaction"] = interaction_extras(q, torch, out, w, dev)
+        # 2-bit rows of the same tables (range), same batches
+        p2 = build_table(q, synth, torch, w, (2,), dev)[2]
+        ms2, _ = bench_bags(q, torch, p2, toff, batches, w, 2, 10, 3, out)
+        b2 = algorithmic_bag_bytes(batches[0]["nnz"], n_bags, w.dim, 2, 4, True)
+        result["int2"] = {"lookups_per_s": batches[0]["nnz"] / (np.mean(ms2) * 1e-3),
+                          "avg_launch_ms": float(np.mean(ms2)),
+                          "GBps": b2 / (np.mean(ms2) * 1e-3) / 1e9,
+                          "hbm_frac": b2 / (np.mean(ms2) * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del p2
         result["device_copy_GBps"] = device_copy_gbps(torch, dev)
         del packed[8]
         torch.cuda.empty_cache()
