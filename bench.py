@@ -35,7 +35,6 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
 VALU_PEAK_OPS = 256 * 64 * 2.4e9  # lane-ops/s: 256 CUs x 64 lanes x 2.4 GHz (no packed fp32)
 HEADLINE_KERNEL = "bag_stream_kernel<4, 8, int, true, true, true>"
-KERNEL_SOURCE = os.path.join(ROOT, "int4_row_wise_amd", "csrc", "qemb.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "bag_stream_int4_multihot_counters.md")
 
 
@@ -78,12 +77,6 @@ def algorithmic_codebook_bytes(nnz: int, n_bags: int, dim: int, idx_bytes: int,
     return nnz * per + (n_bags + 1) * idx_bytes + n_bags * dim * 4
 
 
-def source_sha256(path: str) -> str:
-    import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
-
-
 def measured_traffic():
     """HBM bytes per launch of the headline kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
@@ -99,7 +92,7 @@ def measured_traffic():
     end = text.find("```", start + 7)
     rec = json.loads(text[start + 7:end])
     from int4_row_wise_amd import build as qbuild
-    src = source_sha256(KERNEL_SOURCE)
+    src = qbuild.source_sha256()
     if rec.get("source_sha256") != src or qbuild.built_source_sha256() != src:
         return None
     return 1024.0 * (rec["fetch_kib_per_dispatch"] * rec["fetch_scale"] +

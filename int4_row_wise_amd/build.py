@@ -14,7 +14,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "qemb.hip")
+CSRC = os.path.join(HERE, "csrc")
+SRC = os.path.join(CSRC, "qemb.hip")  # the translation unit; it includes the csrc/*.inc parts
 HEADER = os.path.join(ROOT, "include", "qemb.h")
 LIB = os.path.join(HERE, "libqemb.so")
 LIB_HASH = LIB + ".srchash"  # source sha256 recorded at build time
@@ -36,7 +37,7 @@ def hipcc() -> str:
 def build(force: bool = True, verbose: bool = False) -> str:
     """Compile csrc/qemb.hip into int4_row_wise_amd/libqemb.so."""
     if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(
-            os.path.getmtime(SRC), os.path.getmtime(HEADER)):
+            [os.path.getmtime(f) for f in source_files()] + [os.path.getmtime(HEADER)]):
         return LIB
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
@@ -54,11 +55,21 @@ def build(force: bool = True, verbose: bool = False) -> str:
     return LIB
 
 
+def source_files() -> list:
+    """qemb.hip and the parts it includes, in a fixed order."""
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".inc")))
+
+
 def source_sha256() -> str:
-    """sha256 of the kernel source the library is built from."""
+    """sha256 over the kernel sources the library is built from (each file's
+    name and bytes, in sorted order)."""
     import hashlib
-    with open(SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in source_files():
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def built_source_sha256() -> str | None:
