@@ -205,6 +205,15 @@ def _bag_args(packed, table_offsets, B, dim, indices, offsets, weights, pool_mod
     return T, itype, pool_mode, out, total_rows
 
 
+def _check_rows(packed: torch.Tensor, stride: int, total_rows: int) -> None:
+    """The packed tensor must hold total_rows rows of the expected stride:
+    the kernels index it by that stride, so a mismatch would read past it."""
+    if packed.dim() != 2 or packed.shape[1] != stride:
+        raise ValueError("packed must be [rows, %d] for this dim and row format" % stride)
+    if not 0 <= total_rows <= packed.shape[0]:
+        raise ValueError("total_rows must be within the packed tensor's %d rows" % packed.shape[0])
+
+
 def bag_forward(packed: torch.Tensor, table_offsets: torch.Tensor, B: int, dim: int, bits: int,
                 indices: torch.Tensor, offsets: torch.Tensor, weights: Optional[torch.Tensor] = None,
                 pool_mode: Optional[int] = None, out: Optional[torch.Tensor] = None,
@@ -215,6 +224,7 @@ def bag_forward(packed: torch.Tensor, table_offsets: torch.Tensor, B: int, dim: 
     T, itype, pool_mode, out, total_rows = _bag_args(
         packed, table_offsets, B, dim, indices, offsets, weights, pool_mode, out, err_count,
         total_rows)
+    _check_rows(packed, row_stride(dim, bits), total_rows)
     _check("qemb_bag_forward", load_library().qemb_bag_forward(
         _ptr(packed), total_rows, _ptr(table_offsets), T, B, dim, bits, _ptr(indices),
         _ptr(offsets), indices.numel(), itype, pool_mode, _ptr(weights), _ptr(out),
@@ -232,6 +242,7 @@ def l2_error(x: torch.Tensor, packed: torch.Tensor, bits: int,
     _dev("x", x, torch.float32)
     _dev("packed", packed, torch.uint8)
     rows, dim = x.shape
+    _check_rows(packed, row_stride(dim, bits), rows)
     if workspace is None:
         workspace = torch.empty(l2_error_workspace_bytes(), dtype=torch.uint8, device=x.device)
     if out4 is None:
@@ -297,6 +308,7 @@ def bag_forward_codebook(packed: torch.Tensor, table_offsets: torch.Tensor, B: i
     T, itype, pool_mode, out, total_rows = _bag_args(
         packed, table_offsets, B, dim, indices, offsets, weights, pool_mode, out, err_count,
         total_rows)
+    _check_rows(packed, codebook_row_stride(dim), total_rows)
     _check("qemb_bag_forward_codebook", load_library().qemb_bag_forward_codebook(
         _ptr(packed), total_rows, _ptr(table_offsets), T, B, dim, _ptr(indices), _ptr(offsets),
         indices.numel(), itype, pool_mode, _ptr(weights), _ptr(out), _ptr(err_count),
@@ -311,6 +323,7 @@ def l2_error_codebook(x: torch.Tensor, packed: torch.Tensor,
     _dev("x", x, torch.float32)
     _dev("packed", packed, torch.uint8)
     rows, dim = x.shape
+    _check_rows(packed, codebook_row_stride(dim), rows)
     if workspace is None:
         workspace = torch.empty(l2_error_workspace_bytes(), dtype=torch.uint8, device=x.device)
     if out4 is None:

@@ -181,3 +181,17 @@ def test_baseline_argument_errors(lib):
     assert f(MIS, 10, 16, 4, 0, 0.0, FAKE, None) == -2
     assert f(FAKE, 10, 16, 4, 0, 0.0, MIS, None) == -2
     assert f(None, 0, 16, 4, 2, 0.0, None, None) == 0
+
+
+def test_binding_checks_the_packed_row_width(lib):
+    """The kernels index packed rows by the stride that dim and the row format
+    imply; the binding rejects a tensor of another width or too few rows."""
+    import torch
+    from int4_row_wise_amd import qemb
+    qemb._check_rows(torch.zeros((10, 80), dtype=torch.uint8), 80, 10)
+    with pytest.raises(ValueError):
+        qemb._check_rows(torch.zeros((10, 48), dtype=torch.uint8), 80, 10)
+    with pytest.raises(ValueError):
+        qemb._check_rows(torch.zeros((10, 80), dtype=torch.uint8), 80, 11)
+    with pytest.raises(ValueError):
+        qemb._check_rows(torch.zeros(800, dtype=torch.uint8), 80, 10)
