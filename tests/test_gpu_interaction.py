@@ -50,11 +50,11 @@ def _inputs(g, B, T, dim):
                                    (17, 17), (26, 64), (33, 100), (48, 128), (63, 128), (64, 128),
                                    (64, 127), (64, 4), (65, 128), (40, 129), (100, 64), (26, 256),
                                    (8, 1000), (200, 32), (61, 128), (57, 100), (50, 68),
-                                   (49, 72)])
+                                   (49, 72), (4, 1024), (1024, 8)])
 def test_interaction_matches_oracle(q, T, dim):
     print("interaction T=%d dim=%d" % (T, dim), flush=True)
     g = np.random.default_rng(9000 + T * 31 + dim)
-    B = 37
+    B = 37 if T < 512 else 5  # T = 1024: 2 MB of output per sample
     dense, pooled = _inputs(g, B, T, dim)
     ref, absd = oracle.dot_interaction(dense, pooled)
     got = host(q.dot_interaction(dev(dense), dev(pooled)))
