@@ -119,7 +119,7 @@ def check_sampled_bags(q, w, packed_gpu, bits, omode, bt, out, n_bags, seed, cod
     return assert_pooled_close(got, ref[:, 0, :], absd[:, 0, :], "sampled bags")
 
 
-@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_multi_hot_full(q, bits):
     """64 tables x 1M rows, d=128, range-quantized; batch 16384 per table, bag
     lengths U{1..64}, Zipf(1.05) ids, U(0,1) weights -- the benchmarked call."""
@@ -273,6 +273,27 @@ def test_baselines_quantizer_workload_full(q):
     cb = q.quantize_codebook(x)
     assert np.array_equal(host(cb[dev(sample)]), oracle.quantize_codebook(xs))
     del cb, x
+    torch.cuda.empty_cache()
+
+
+def test_int2_table_over_2gb_takes_64bit_addressing(q):
+    """2-bit rows of d=128 (48 bytes) in a table of 46M rows (2.2 GB) beside
+    a small one, multi-hot bags: the rows of the large table are read with
+    64-bit addresses.  Sampled bags against the oracle, counts exact."""
+    import torch
+    w = synth.scaled(synth.workload(4), rows=(46_000_000, 1000), batch=2000)
+    print("int2 table over 2 GB", flush=True)
+    bt = synth.batch(w, batch_seed=1, index_dtype=np.int64)
+    far = int(np.sum(bt.indices[: bt.offsets[bt.B]] >= (1 << 31) // 48))
+    assert far > 100  # ids past the first 2 GB of the table
+    packed = pack_tables(q, w, 2, q.RANGE)
+    assert packed.shape[1] * w.rows[0] > (1 << 31)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = host(q.bag_forward(packed, dev(bt.table_offsets), bt.B, w.dim, 2, dev(bt.indices),
+                             dev(bt.offsets), dev(bt.weights), err_count=err))
+    assert int(host(err)[0]) == 0
+    check_sampled_bags(q, w, packed, 2, oracle.RANGE, bt, out, 300, 97)
+    del packed
     torch.cuda.empty_cache()
 
 

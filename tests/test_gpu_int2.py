@@ -74,6 +74,31 @@ def test_int2_bag_ragged(q, dim, weighted):
     assert np.all(got[empty] == 0) and not np.any(np.signbit(got[empty]))
 
 
+@pytest.mark.parametrize("dim", [1, 16, 33, 64, 128, 200])
+def test_int2_bag_short(q, dim):
+    """Bags of 0..6 ids (fewer than 8 on average take the one-wave-per-bag
+    kernel at every width), int64 ids, weighted."""
+    import torch
+    g = np.random.default_rng(11250 + dim)
+    rows = [40, 3, 500]
+    x = special_rows(g, sum(rows), dim)
+    x[np.abs(x) > 100] = 1.0
+    packed = oracle.quantize_rowwise(x, 2, oracle.GREEDY, 200, 100)
+    T, B = 3, 211
+    lengths = g.integers(0, 7, size=T * B)
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    idx = np.concatenate([g.integers(0, rows[gb // B], size=lengths[gb]) for gb in range(T * B)])
+    idx = idx.astype(np.int64)
+    w = g.random(idx.size).astype(np.float32)
+    toff = np.concatenate([[0], np.cumsum(rows)]).astype(np.int64)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = host(q.bag_forward(dev(packed), dev(toff), B, dim, 2, dev(idx), dev(offsets), dev(w),
+                             err_count=err))
+    ref, absd, rerr = oracle.bag_forward(packed, toff, B, dim, 2, idx, offsets, w)
+    assert int(host(err)[0]) == rerr == 0
+    assert_pooled_close(got, ref, absd, "int2 short dim %d" % dim)
+
+
 def test_int2_bag_invalid_and_multi_hot(q):
     import torch
     g = np.random.default_rng(11300)
