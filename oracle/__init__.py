@@ -18,7 +18,11 @@ pages it follows, is stated in the C source:
   method"), summed in binary64;
 * the normalized l2 error (Post-Training 4-bit page, "Proposed method");
 * codebook rows: 16 fp32 levels per row from 1-D k-means and 4-bit codes
-  (Post-Training 4-bit page, "Proposed method" and "Main findings").
+  (Post-Training 4-bit page, "Proposed method" and "Main findings");
+* error-bounded compression of the pooled embeddings devices exchange
+  ("Avancées dans les recommandations en Deep Learning", scisimple page,
+  "Méthodes de Compression des Données", "Stratégies de Compression
+  Adaptative").
 """
 from __future__ import annotations
 
@@ -102,6 +106,14 @@ def lib() -> ctypes.CDLL:
         L.oracle_interaction_width.restype = i64
         L.oracle_dot_interaction.argtypes = [p, p, i64, i32, i32, p, p]
         L.oracle_dot_interaction.restype = i32
+        L.oracle_record_bytes.argtypes = [i32, i32]
+        L.oracle_record_bytes.restype = i64
+        L.oracle_compress_bound.argtypes = [i64, i32]
+        L.oracle_compress_bound.restype = i64
+        L.oracle_compress_pooled.argtypes = [p, i64, i32, i32, p, p, p, p]
+        L.oracle_compress_pooled.restype = i32
+        L.oracle_decompress_pooled.argtypes = [p, i64, p, i64, i32, i32, p, p, p]
+        L.oracle_decompress_pooled.restype = i32
         _lib = L
     return _lib
 
@@ -362,3 +374,50 @@ def quantize_baseline(x: np.ndarray, bits: int, method: int, param: float = 0.0)
     if rc != 0:
         raise OracleError("oracle_quantize_baseline returned %d" % rc)
     return packed
+
+
+RAW_WIDTH = 32  # record header of a vector stored verbatim
+
+
+def record_bytes(dim: int, w: int) -> int:
+    return int(lib().oracle_record_bytes(dim, w))
+
+
+def compress_bound(n: int, dim: int) -> int:
+    return int(lib().oracle_compress_bound(n, dim))
+
+
+def compress_pooled(x: np.ndarray, eb: np.ndarray):
+    """x: [B][T][d] (or [n][d] with T = len(eb)) fp32 pooled vectors; eb: [T]
+    per-table bounds.  Returns (buf uint8 [offs[-1]], offs int64 [n + 1],
+    widths int32 [n])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    eb = np.ascontiguousarray(eb, dtype=np.float32).reshape(-1)
+    T = eb.size
+    dim = x.shape[-1]
+    n = x.size // dim if dim else 0
+    if x.ndim == 3:
+        assert x.shape[1] == T, (x.shape, T)
+    out = np.zeros(max(compress_bound(n, dim), 1), dtype=np.uint8)
+    offs = np.zeros(n + 1, dtype=np.int64)
+    widths = np.zeros(max(n, 1), dtype=np.int32)
+    rc = lib().oracle_compress_pooled(_ptr(x), n, dim, T, _ptr(eb), _ptr(out), _ptr(offs), _ptr(widths))
+    if rc != 0:
+        raise OracleError("oracle_compress_pooled returned %d" % rc)
+    return out[: offs[-1]].copy(), offs, widths[:n]
+
+
+def decompress_pooled(buf: np.ndarray, offs: np.ndarray, dim: int, eb: np.ndarray):
+    """Inverse of compress_pooled: returns (y fp32 [n][d], number of bad
+    records)."""
+    buf = np.ascontiguousarray(buf, dtype=np.uint8)
+    offs = np.ascontiguousarray(offs, dtype=np.int64)
+    eb = np.ascontiguousarray(eb, dtype=np.float32).reshape(-1)
+    n = offs.size - 1
+    y = np.zeros((max(n, 0), dim), dtype=np.float32)
+    bad = np.zeros(1, dtype=np.int64)
+    rc = lib().oracle_decompress_pooled(_ptr(buf) if buf.size else None, buf.size, _ptr(offs), n, dim,
+                                        eb.size, _ptr(eb), _ptr(y), _ptr(bad))
+    if rc != 0:
+        raise OracleError("oracle_decompress_pooled returned %d" % rc)
+    return y, int(bad[0])

@@ -44,6 +44,14 @@
  *    (T+1) x d matrix Z; the output is the dense vector followed by
  *    <z_i, z_j> for every pair 0 <= j < i <= T, row by row.
  *
+ *  - Error-bounded lossy compression of the pooled embeddings that devices
+ *    exchange ("Avancées dans les recommandations en Deep Learning",
+ *    scisimple page, "Méthodes de Compression des Données" and "Stratégies
+ *    de Compression Adaptative": a user-set maximum error, one per table):
+ *    a uniform quantizer of bin width twice the bound, zigzag codes packed
+ *    at each vector's bit width, vectors that cannot meet the bound stored
+ *    verbatim.
+ *
  * The pages give no formulas.  The numeric rules used here (binary32 RNE with
  * one rounding per written operation, no contraction, IEEE division, fp16
  * round-to-nearest-even, ties-to-even code rounding, the contiguous-halves
@@ -889,5 +897,181 @@ int oracle_dot_interaction(const float* dense, const float* pooled, int64_t B, i
       }
     }
   }
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Error-bounded compression of pooled embeddings.                      */
+/* ------------------------------------------------------------------ */
+
+/* "Avancées dans les recommandations en Deep Learning" (scisimple page,
+   sections "Défis de Communication", "Méthodes de Compression des Données"
+   and "Stratégies de Compression Adaptative"): the embeddings that devices
+   exchange in the all-to-all are compressed by a lossy method whose
+   reconstruction error stays within a bound the user sets, and each table
+   may have a bound of its own.  The page names no scheme; the reading here
+   is the plainest error-bounded one, a uniform quantizer of bin width twice
+   the bound followed by a fixed-width bit packing of each vector's codes:
+
+     step = 2 eb (binary32), q = rint(x / step) (IEEE division, ties to even),
+     x' = step * (float)q (binary32), kept only if |x - x'| <= eb;
+     u = 2q for q >= 0, -2q - 1 for q < 0 (zigzag), w = bit length of the
+     vector's largest u (0 .. 31), element i's u at bits [i w, i w + w) of a
+     little-endian bit stream of dwords.
+
+   A vector with a non-finite element, a |q| >= 2^30 or an element that
+   misses the bound, or whose table's eb is not a positive finite number
+   (or makes step infinite), is stored verbatim (header 32).  The bound then
+   holds for every element of every vector.
+
+   Record of a vector: a uint32 header (w, or 32 for a verbatim vector), then
+   ceil(d w / 32) payload dwords (d fp32 values when verbatim).  Vector v of
+   n = B T (the [B][T][d] order of the lookup's output) uses the bound of
+   table v mod T.  Records follow each other in vector order; offs[v] is the
+   byte offset of record v, offs[0] = 0 and offs[n] the total size. */
+#define OR_RAW_W 32
+
+int64_t oracle_record_bytes(int dim, int w) {
+  if (dim < 1 || w < 0 || w > OR_RAW_W) return -1;
+  if (w == OR_RAW_W) return 4 + 4 * (int64_t)dim;
+  return 4 + 4 * (((int64_t)dim * w + 31) / 32);
+}
+
+int64_t oracle_compress_bound(int64_t n, int dim) {
+  if (n < 0 || dim < 1) return -1;
+  return n * oracle_record_bytes(dim, OR_RAW_W);
+}
+
+static uint32_t zigzag(int32_t q) {
+  return q >= 0 ? 2u * (uint32_t)q : 2u * (uint32_t)(-(int64_t)q) - 1u;
+}
+
+static int32_t unzigzag(uint32_t u) {
+  return (u & 1u) ? -(int32_t)((u - 1u) / 2u) - 1 : (int32_t)(u / 2u);
+}
+
+static int bit_length(uint32_t v) {
+  int w = 0;
+  while (v) {
+    ++w;
+    v >>= 1;
+  }
+  return w;
+}
+
+/* The width of a vector (0 .. 31), or OR_RAW_W if it is stored verbatim;
+   u[i] receives the zigzag codes when it is not. */
+static int vector_width(const float* x, int d, float eb, uint32_t* u) {
+  if (!(eb > 0.0f) || !isfinite(eb)) return OR_RAW_W;
+  const float step = 2.0f * eb;
+  if (!isfinite(step)) return OR_RAW_W;
+  uint32_t umax = 0;
+  for (int i = 0; i < d; ++i) {
+    if (!isfinite(x[i])) return OR_RAW_W;
+    const float r = rintf(x[i] / step);
+    if (!(fabsf(r) < 1073741824.0f)) return OR_RAW_W; /* |q| < 2^30 */
+    const int32_t q = (int32_t)r;
+    const float xr = step * (float)q;
+    if (!(fabsf(x[i] - xr) <= eb)) return OR_RAW_W;
+    u[i] = zigzag(q);
+    if (u[i] > umax) umax = u[i];
+  }
+  return bit_length(umax);
+}
+
+static void put_u32(uint8_t* p, uint32_t v) {
+  for (int k = 0; k < 4; ++k) p[k] = (uint8_t)(v >> (8 * k));
+}
+
+static uint32_t get_u32(const uint8_t* p) {
+  return (uint32_t)p[0] | (uint32_t)p[1] << 8 | (uint32_t)p[2] << 16 | (uint32_t)p[3] << 24;
+}
+
+/* x: [n][dim] fp32 (vector v of table v mod T); eb: [T]; out: at least
+   oracle_compress_bound(n, dim) bytes, of which offs[n] are written;
+   offs: [n + 1].  widths (nullable): [n], each vector's header. */
+int oracle_compress_pooled(const float* x, int64_t n, int dim, int T, const float* eb,
+                           uint8_t* out, int64_t* offs, int32_t* widths) {
+  if (n < 0 || dim < 1 || dim > OR_MAX_DIM || T < 1 || (n > 0 && (!x || !eb || !out)) || !offs)
+    return OR_INVALID;
+  int32_t* w = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  if (!w) return OR_INVALID;
+#pragma omp parallel
+  {
+    uint32_t* u = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)dim);
+#pragma omp for schedule(static)
+    for (int64_t v = 0; v < n; ++v) w[v] = vector_width(x + v * dim, dim, eb[v % T], u);
+    free(u);
+  }
+  offs[0] = 0;
+  for (int64_t v = 0; v < n; ++v) offs[v + 1] = offs[v] + oracle_record_bytes(dim, w[v]);
+#pragma omp parallel
+  {
+    uint32_t* u = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)dim);
+#pragma omp for schedule(static)
+    for (int64_t v = 0; v < n; ++v) {
+      const float* xv = x + v * dim;
+      uint8_t* rec = out + offs[v];
+      put_u32(rec, (uint32_t)w[v]);
+      if (w[v] == OR_RAW_W) {
+        memcpy(rec + 4, xv, 4 * (size_t)dim);
+        continue;
+      }
+      vector_width(xv, dim, eb[v % T], u);
+      const int64_t nbytes = oracle_record_bytes(dim, w[v]) - 4;
+      memset(rec + 4, 0, (size_t)nbytes);
+      for (int i = 0; i < dim; ++i)
+        for (int k = 0; k < w[v]; ++k)
+          if ((u[i] >> k) & 1u) {
+            const int64_t bit = (int64_t)i * w[v] + k;
+            rec[4 + bit / 8] |= (uint8_t)(1u << (bit % 8));
+          }
+    }
+    free(u);
+  }
+  if (widths)
+    for (int64_t v = 0; v < n; ++v) widths[v] = w[v];
+  free(w);
+  return OR_OK;
+}
+
+/* Inverse of oracle_compress_pooled.  in: in_bytes bytes; offs: [n + 1];
+   y: [n][dim].  A record whose offsets are out of order or outside
+   [0, in_bytes], whose header exceeds 32, or whose size differs from what
+   its header implies, is decoded as zeros and counted in *n_bad. */
+int oracle_decompress_pooled(const uint8_t* in, int64_t in_bytes, const int64_t* offs, int64_t n,
+                             int dim, int T, const float* eb, float* y, int64_t* n_bad) {
+  if (n < 0 || dim < 1 || dim > OR_MAX_DIM || T < 1 || in_bytes < 0 || !offs ||
+      (n > 0 && (!eb || !y)) || (in_bytes > 0 && !in))
+    return OR_INVALID;
+  int64_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : bad)
+  for (int64_t v = 0; v < n; ++v) {
+    float* yv = y + v * dim;
+    const int64_t a = offs[v], b = offs[v + 1];
+    int ok = a >= 0 && a <= b && b <= in_bytes && b - a >= 4;
+    uint32_t hdr = ok ? get_u32(in + a) : 0;
+    ok = ok && hdr <= OR_RAW_W && b - a == oracle_record_bytes(dim, (int)hdr);
+    if (!ok) {
+      for (int i = 0; i < dim; ++i) yv[i] = 0.0f;
+      ++bad;
+      continue;
+    }
+    const uint8_t* p = in + a + 4;
+    if (hdr == OR_RAW_W) {
+      memcpy(yv, p, 4 * (size_t)dim);
+      continue;
+    }
+    const float step = 2.0f * eb[v % T];
+    for (int i = 0; i < dim; ++i) {
+      uint32_t uu = 0;
+      for (int k = 0; k < (int)hdr; ++k) {
+        const int64_t bit = (int64_t)i * hdr + k;
+        uu |= (uint32_t)((p[bit / 8] >> (bit % 8)) & 1u) << k;
+      }
+      yv[i] = step * (float)unzigzag(uu);
+    }
+  }
+  if (n_bad) *n_bad = bad;
   return OR_OK;
 }
