@@ -913,16 +913,21 @@ int oracle_dot_interaction(const float* dense, const float* pooled, int64_t B, i
    is the plainest error-bounded one, a uniform quantizer of bin width twice
    the bound followed by a fixed-width bit packing of each vector's codes:
 
-     step = 2 eb (binary32), q = rint(x / step) (IEEE division, ties to even),
-     x' = step * (float)q (binary32), kept only if |x - x'| <= eb;
+     step = 2 eb, inv = 1 / step (IEEE division, once per table),
+     q = rint(x * inv) (ties to even), x' = step * (float)q, all binary32,
+     kept only if |x - x'| <= eb;
      u = 2q for q >= 0, -2q - 1 for q < 0 (zigzag), w = bit length of the
      vector's largest u (0 .. 31), element i's u at bits [i w, i w + w) of a
      little-endian bit stream of dwords.
 
-   A vector with a non-finite element, a |q| >= 2^30 or an element that
-   misses the bound, or whose table's eb is not a positive finite number
-   (or makes step infinite), is stored verbatim (header 32).  The bound then
-   holds for every element of every vector.
+   The code is taken against the reciprocal of the bin width, as the
+   row-wise quantizer takes its codes against the reciprocal of the stored
+   scale; the check that follows catches the rare element that this
+   rounding (or any other) puts past the bound.  A vector with a non-finite
+   element, a |q| >= 2^30 or an element that misses the bound, or whose
+   table's eb is not a positive finite number (or makes step infinite), is
+   stored verbatim (header 32).  The bound then holds for every element of
+   every vector.
 
    Record of a vector: a uint32 header (w, or 32 for a verbatim vector), then
    ceil(d w / 32) payload dwords (d fp32 values when verbatim).  Vector v of
@@ -965,10 +970,11 @@ static int vector_width(const float* x, int d, float eb, uint32_t* u) {
   if (!(eb > 0.0f) || !isfinite(eb)) return OR_RAW_W;
   const float step = 2.0f * eb;
   if (!isfinite(step)) return OR_RAW_W;
+  const float inv = 1.0f / step;
   uint32_t umax = 0;
   for (int i = 0; i < d; ++i) {
     if (!isfinite(x[i])) return OR_RAW_W;
-    const float r = rintf(x[i] / step);
+    const float r = rintf(x[i] * inv);
     if (!(fabsf(r) < 1073741824.0f)) return OR_RAW_W; /* |q| < 2^30 */
     const int32_t q = (int32_t)r;
     const float xr = step * (float)q;
