@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--codebook-only", action="store_true",
                     help="only the codebook-row lookup of the multi-hot workload (for profiling)")
+    ap.add_argument("--compress-only", action="store_true",
+                    help="error-bounded compression of the pooled output only")
     ap.add_argument("--interaction-only", action="store_true",
                     help="only one INT4 lookup and the dot interaction on its output (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -407,6 +409,46 @@ def interaction_extras(q, torch, pooled, w, dev, steps=20, warmup=3):
             "useful_TFLOPs": useful / (ms * 1e-3) / 1e12, "bytes_per_launch": byt}
 
 
+def compress_extras(q, torch, pooled, dev, steps=20, warmup=3):
+    """Error-bounded compression of the lookup's pooled output (the payload a
+    table-sharded model sends in its all-to-all) and its inverse.  The pages
+    give no bound; each table's bound is 1 % of the standard deviation of its
+    pooled values.  Algorithmic bytes: compression reads every vector once and
+    writes the records and offsets; decompression reads the records and
+    offsets and writes every vector."""
+    B, T, dim = pooled.shape
+    n = B * T
+    eb = (0.01 * pooled.std(dim=(0, 2))).float().contiguous()
+    buf = torch.empty(q.compress_bound(n, dim), dtype=torch.uint8, device=dev)
+    offs = torch.empty(n + 1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(q.compress_workspace_bytes(n), 16), dtype=torch.uint8, device=dev)
+    y = torch.empty((n, dim), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        q.compress_pooled(pooled, eb, out=buf, offs=offs, workspace=ws)
+        q.decompress_pooled(buf, offs, dim, eb, y=y)
+    torch.cuda.synchronize()
+    total = int(offs[-1].item())
+    tc, td = Timer(torch), Timer(torch)
+    for _ in range(steps):
+        with tc:
+            q.compress_pooled(pooled, eb, out=buf, offs=offs, workspace=ws)
+    for _ in range(steps):
+        with td:
+            q.decompress_pooled(buf, offs, dim, eb, y=y, in_bytes=total)
+    msc, msd = float(np.mean(tc.ms())), float(np.mean(td.ms()))
+    err = float((y.view(B, T, dim) - pooled).abs().div(eb.view(1, T, 1)).max().item())
+    raw = n * dim * 4
+    bc = raw + total + 8 * (n + 1)
+    bd = total + 8 * (n + 1) + raw
+    return {"vectors": n, "dim": dim, "tables": T, "bound": "1 % of each table's std",
+            "compressed_bytes": total, "ratio": raw / total, "max_err_over_bound": err,
+            "compress_ms": msc, "compress_GBps": bc / (msc * 1e-3) / 1e9,
+            "compress_hbm_frac": bc / (msc * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "decompress_ms": msd, "decompress_GBps": bd / (msd * 1e-3) / 1e9,
+            "decompress_hbm_frac": bd / (msd * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "compress_bytes_per_call": bc, "decompress_bytes_per_call": bd}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -434,7 +476,7 @@ def main():
     q.load_library()
     dev = torch.device("cuda:0")
     w = synth.workload(4)
-    bits_list = (4,) if (args.no_extras or args.interaction_only) else (4, 8)
+    bits_list = (4,) if (args.no_extras or args.interaction_only or args.compress_only) else (4, 8)
 
     t0 = time.time()
     packed = {} if args.codebook_only else build_table(q, synth, torch, w, bits_list, dev)
@@ -451,11 +493,15 @@ def main():
         len(batches), time.time() - t0, [b["nnz"] for b in batches]))
     n_bags = w.n_tables * w.batch
     out = torch.empty((w.batch, w.n_tables, w.dim), dtype=torch.float32, device=dev)
-    if args.interaction_only:
+    if args.interaction_only or args.compress_only:
         b0 = batches[0]
         q.bag_forward(packed[4], toff, w.batch, w.dim, 4, b0["idx"], b0["offs"], b0["w"], out=out)
-        res = interaction_extras(q, torch, out, w, dev, args.steps, args.warmup)
-        print(json.dumps({"interaction": res, "workload": w.name}), flush=True)
+        if args.compress_only:
+            res = compress_extras(q, torch, out, dev, args.steps, args.warmup)
+            print(json.dumps({"compress": res, "workload": w.name}), flush=True)
+        else:
+            res = interaction_extras(q, torch, out, w, dev, args.steps, args.warmup)
+            print(json.dumps({"interaction": res, "workload": w.name}), flush=True)
         return
     if args.codebook_only:
         del packed
@@ -534,6 +580,7 @@ def main():
             "launch_ms": launch_stats(msc), "GBps": b0 / (np.median(msc) * 1e-3) / 1e9,
             "hbm_frac": b0 / (np.median(msc) * 1e-3) / 1e9 / HBM_PEAK_GBS}
         result["interaction"] = interaction_extras(q, torch, out, w, dev)
+        result["compress"] = compress_extras(q, torch, out, dev)
         # 2-bit rows of the same tables (range), same batches
         p2 = build_table(q, synth, torch, w, (2,), dev)[2]
         ms2, _ = bench_bags(q, torch, p2, toff, batches, w, 2, 10, 3, out)

@@ -89,6 +89,8 @@ typedef struct ihipStream_t* qemb_stream_t; /* the same type as hipStream_t */
 #define QEMB_CLIP_RANGE 0
 #define QEMB_CLIP_GREEDY 1
 
+#define QEMB_COMPRESS_VERBATIM 32 /* record header of a vector stored verbatim */
+
 #define QEMB_BASE_SYMMETRIC 0
 #define QEMB_BASE_PERCENTILE 1
 #define QEMB_BASE_ACIQ 2
@@ -293,6 +295,62 @@ int qemb_l2_error_codebook(const float* x, const uint8_t* packed, int64_t rows, 
 int64_t qemb_interaction_width(int32_t T, int32_t dim);
 int qemb_dot_interaction(const float* dense, const float* pooled, int64_t B, int32_t T,
                          int32_t dim, float* out, qemb_stream_t stream);
+
+/*
+ * Error-bounded compression of pooled vectors, the payload a table-sharded
+ * model exchanges in its all-to-all ("Avancées dans les recommandations en
+ * Deep Learning", scisimple page, "Méthodes de Compression des Données": a
+ * lossy method whose reconstruction error stays within a maximum the user
+ * sets; "Stratégies de Compression Adaptative": one bound per table, which
+ * may change from call to call).  Per element, in binary32 with one
+ * rounding per operation:
+ *   step = 2 eb, inv = 1 / step (IEEE division, once per vector),
+ *   q = rint(x * inv) (ties to even), x' = step * (float)q, and
+ *   |x - x'| <= eb is checked;
+ *   u = 2q for q >= 0, -2q - 1 for q < 0.
+ * A vector's width w (0 .. 31) is the bit length of its largest u; element i's
+ * u sits at bits [i w, i w + w) of a little-endian stream of dwords.  A vector
+ * with an element that is not finite, has |q| >= 2^30 or misses the bound
+ * after rounding, or whose table's eb is not a positive finite number (or
+ * makes step overflow), is stored verbatim instead: every decompressed
+ * element is then within eb of the input (verbatim ones bit-exact), and the
+ * decompressed zeros of coded vectors are +0.
+ * Record of a vector: a uint32 header (w, or QEMB_COMPRESS_VERBATIM), then
+ * ceil(dim w / 32) payload dwords, or dim fp32 values for a verbatim one;
+ * qemb_compress_record_bytes gives its size.  Records follow in vector order.
+ *
+ * qemb_compress_pooled
+ *   x     [n][dim] fp32, 16-byte aligned; vector v belongs to table v mod T
+ *         (the [B][T][dim] output of qemb_bag_forward has n = B T)
+ *   eb    [T] fp32 device array (4-byte aligned), the tables' bounds
+ *   out   device buffer of qemb_compress_bound(n, dim) bytes, 4-byte aligned;
+ *         the first offs[n] bytes are written
+ *   offs  [n + 1] int64 device array, 8-byte aligned: offs[v] is the byte
+ *         offset of record v, offs[0] = 0, offs[n] the total size (the rank
+ *         chunk [v0, v1) of an all-to-all is bytes [offs[v0], offs[v1]))
+ *   workspace  qemb_compress_workspace_bytes(n) bytes of device memory,
+ *         16-byte aligned, owned by the caller (contents need no clearing)
+ *   n >= 0 (0 writes offs[0] = 0), 1 <= dim <= QEMB_MAX_DIM, T >= 1
+ * Deterministic and bit-exact; three kernel launches on the stream.
+ *
+ * qemb_decompress_pooled
+ *   in    in_bytes bytes of records, 4-byte aligned; offs [n + 1] as written
+ *         by the compressor (relative to in); eb the same bounds
+ *   y     [n][dim] fp32, 16-byte aligned, fully written
+ *   err_count  device int32, nullable, incremented (the caller zeroes it)
+ *         once per malformed record: offsets out of order or outside
+ *         [0, in_bytes], a header above 32, or a size that differs from
+ *         what the header implies; such a vector is written as zeros.  No
+ *         read leaves [in, in + in_bytes).
+ */
+int64_t qemb_compress_record_bytes(int32_t dim, int32_t w);
+int64_t qemb_compress_bound(int64_t n, int32_t dim);
+size_t qemb_compress_workspace_bytes(int64_t n);
+int qemb_compress_pooled(const float* x, int64_t n, int32_t dim, int32_t T, const float* eb,
+                         uint8_t* out, int64_t* offs, void* workspace, qemb_stream_t stream);
+int qemb_decompress_pooled(const uint8_t* in, int64_t in_bytes, const int64_t* offs, int64_t n,
+                           int32_t dim, int32_t T, const float* eb, float* y, int32_t* err_count,
+                           qemb_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -12,4 +12,6 @@ from .qemb import (  # noqa: F401
     bag_forward_codebook, codebook_row_stride, dequantize, dequantize_codebook, dot_interaction,
     interaction_width, l2_error,
     l2_error_codebook, load_library, quantize_codebook, quantize_rowwise, row_stride,
+    COMPRESS_VERBATIM, compress_bound, compress_pooled, compress_record_bytes, compress_workspace_bytes,
+    decompress_pooled,
 )

@@ -10,6 +10,7 @@
 //   * bag_wave_kernel         the same for rows wider than 8 lanes
 //   * bag_slice_kernel        the same for short bags, several bags per wave
 //   * l2_partial/l2_final     normalized l2 error, fixed-order reduction
+//   * compress_* / decompress error-bounded compression of pooled vectors
 //
 // The method: row-wise uniform quantization with fp16 scale and bias, clip
 // thresholds from the row range or from a greedy search over the squared
@@ -44,6 +45,7 @@ constexpr int kBlock = 256;
 #include "codebook.inc"
 #include "lookup_int2.inc"
 #include "interaction.inc"
+#include "compress.inc"
 #include "host.inc"
 
 }  // namespace
@@ -323,6 +325,52 @@ int qemb_l2_error(const float* x, const uint8_t* packed, int64_t rows, int32_t d
   if (launched() != QEMB_OK) return QEMB_E_LAUNCH;
   hipLaunchKernelGGL(l2_final_kernel, dim3(1), dim3(kBlock), 0, st, part, out4);
   return launched();
+}
+
+int64_t qemb_compress_record_bytes(int32_t dim, int32_t w) {
+  if (dim < 1 || dim > QEMB_MAX_DIM || w < 0 || w > QEMB_COMPRESS_VERBATIM) return -1;
+  return 4 + 4 * (w == QEMB_COMPRESS_VERBATIM ? (int64_t)dim : ((int64_t)dim * w + 31) / 32);
+}
+
+int64_t qemb_compress_bound(int64_t n, int32_t dim) {
+  if (n < 0 || dim < 1 || dim > QEMB_MAX_DIM || n > INT64_MAX / (4 + 4 * (int64_t)dim)) return -1;
+  return n * (4 + 4 * (int64_t)dim);
+}
+
+size_t qemb_compress_workspace_bytes(int64_t n) {
+  if (n < 0) return 0;
+  const int64_t nblk = (n + kCmpVPB - 1) / kCmpVPB;
+  return (size_t)(8 * nblk + ((n + 15) / 16) * 16);
+}
+
+int qemb_compress_pooled(const float* x, int64_t n, int32_t dim, int32_t T, const float* eb,
+                         uint8_t* out, int64_t* offs, void* workspace, qemb_stream_t stream) {
+  if (n < 0 || dim < 1 || T < 1) return QEMB_E_INVALID_ARG;
+  if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
+  if (!offs || (n > 0 && (!x || !eb || !out || !workspace))) return QEMB_E_INVALID_ARG;
+  if ((x && !aligned16(x)) || ((uintptr_t)out & 3u) || ((uintptr_t)offs & 7u) ||
+      ((uintptr_t)eb & 3u) || (workspace && !aligned16(workspace)))
+    return QEMB_E_MISALIGNED;
+  const int64_t nblk = (n + kCmpVPB - 1) / kCmpVPB;
+  if (nblk > 0x7fffffff) return QEMB_E_UNSUPPORTED;
+  int64_t* bsum = reinterpret_cast<int64_t*>(workspace);
+  uint8_t* wbuf = reinterpret_cast<uint8_t*>(workspace) + 8 * nblk;
+  return dispatch_compress(x, n, dim, T, eb, out, offs, bsum, wbuf, reinterpret_cast<hipStream_t>(stream));
+}
+
+int qemb_decompress_pooled(const uint8_t* in, int64_t in_bytes, const int64_t* offs, int64_t n,
+                           int32_t dim, int32_t T, const float* eb, float* y, int32_t* err_count,
+                           qemb_stream_t stream) {
+  if (n < 0 || dim < 1 || T < 1 || in_bytes < 0) return QEMB_E_INVALID_ARG;
+  if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
+  if (n == 0) return QEMB_OK;
+  if (!offs || !eb || !y || (in_bytes > 0 && !in)) return QEMB_E_INVALID_ARG;
+  if (((uintptr_t)in & 3u) || ((uintptr_t)offs & 7u) || ((uintptr_t)eb & 3u) || !aligned16(y))
+    return QEMB_E_MISALIGNED;
+  const int64_t nblk = (n + kCmpVPB - 1) / kCmpVPB;
+  if (nblk > 0x7fffffff) return QEMB_E_UNSUPPORTED;
+  return dispatch_decompress(in, in_bytes, offs, n, dim, T, eb, y, err_count,
+                             reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -27,8 +27,12 @@ EXPORTED = (
     "qemb_dequantize", "qemb_bag_forward", "qemb_l2_error_workspace_bytes", "qemb_l2_error",
     "qemb_codebook_row_stride", "qemb_quantize_codebook", "qemb_dequantize_codebook",
     "qemb_bag_forward_codebook", "qemb_l2_error_codebook", "qemb_interaction_width",
-    "qemb_dot_interaction", "qemb_quantize_baseline",
+    "qemb_dot_interaction", "qemb_quantize_baseline", "qemb_compress_record_bytes",
+    "qemb_compress_bound", "qemb_compress_workspace_bytes", "qemb_compress_pooled",
+    "qemb_decompress_pooled",
 )
+
+COMPRESS_VERBATIM = 32  # record header of a vector stored verbatim
 
 SYMMETRIC, PERCENTILE, ACIQ = 0, 1, 2
 
@@ -83,6 +87,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.qemb_interaction_width.restype = i64
     L.qemb_dot_interaction.argtypes = [p, p, i64, i32, i32, p, p]
     L.qemb_dot_interaction.restype = ctypes.c_int
+    L.qemb_compress_record_bytes.argtypes = [i32, i32]
+    L.qemb_compress_record_bytes.restype = i64
+    L.qemb_compress_bound.argtypes = [i64, i32]
+    L.qemb_compress_bound.restype = i64
+    L.qemb_compress_workspace_bytes.argtypes = [i64]
+    L.qemb_compress_workspace_bytes.restype = ctypes.c_size_t
+    L.qemb_compress_pooled.argtypes = [p, i64, i32, i32, p, p, p, p, p]
+    L.qemb_compress_pooled.restype = ctypes.c_int
+    L.qemb_decompress_pooled.argtypes = [p, i64, p, i64, i32, i32, p, p, p, p]
+    L.qemb_decompress_pooled.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -363,3 +377,86 @@ def dot_interaction(dense: torch.Tensor, pooled: torch.Tensor,
     _check("qemb_dot_interaction", load_library().qemb_dot_interaction(
         _ptr(dense), _ptr(pooled), B, T, dim, _ptr(out), _stream(dense)))
     return out
+
+
+# ---- error-bounded compression of pooled vectors (the all-to-all payload) ----
+
+def compress_record_bytes(dim: int, w: int) -> int:
+    r = int(load_library().qemb_compress_record_bytes(dim, w))
+    if r < 0:
+        raise ValueError("unsupported dim=%d w=%d" % (dim, w))
+    return r
+
+
+def compress_bound(n: int, dim: int) -> int:
+    r = int(load_library().qemb_compress_bound(n, dim))
+    if r < 0:
+        raise ValueError("unsupported n=%d dim=%d" % (n, dim))
+    return r
+
+
+def compress_workspace_bytes(n: int) -> int:
+    return int(load_library().qemb_compress_workspace_bytes(n))
+
+
+def _vectors(x: torch.Tensor, T: Optional[int]):
+    if x.dim() == 3:
+        if T is not None and T != x.shape[1]:
+            raise ValueError("T=%d does not match x of shape %s" % (T, tuple(x.shape)))
+        return x.shape[0] * x.shape[1], x.shape[1], x.shape[2]
+    if x.dim() != 2 or T is None:
+        raise ValueError("x must be [B, T, d], or [n, d] with T given")
+    return x.shape[0], T, x.shape[1]
+
+
+def compress_pooled(x: torch.Tensor, eb: torch.Tensor, T: Optional[int] = None,
+                    out: Optional[torch.Tensor] = None, offs: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None):
+    """Error-bounded compression of pooled vectors x ([B, T, d], or [n, d]
+    with T) under the per-table bounds eb ([T] float32, device).  Returns
+    (out, offs): out is a uint8 buffer of compress_bound(n, d) bytes whose
+    first offs[-1] bytes hold the records; offs is int64 [n + 1] on the
+    device (reading offs[-1] on the host synchronizes)."""
+    _dev("x", x, torch.float32)
+    _dev("eb", eb, torch.float32)
+    n, T, dim = _vectors(x, T)
+    if eb.numel() != T:
+        raise ValueError("eb must hold %d bounds" % T)
+    if out is None:
+        out = torch.empty(max(compress_bound(n, dim), 1), dtype=torch.uint8, device=x.device)
+    if offs is None:
+        offs = torch.empty(n + 1, dtype=torch.int64, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(compress_workspace_bytes(n), 16), dtype=torch.uint8, device=x.device)
+    _dev("out", out, torch.uint8)
+    _dev("offs", offs, torch.int64)
+    _dev("workspace", workspace, torch.uint8)
+    if out.numel() < compress_bound(n, dim) or offs.numel() != n + 1 or \
+            workspace.numel() < compress_workspace_bytes(n):
+        raise ValueError("out, offs or workspace too small")
+    _check("qemb_compress_pooled", load_library().qemb_compress_pooled(
+        _ptr(x), n, dim, T, _ptr(eb), _ptr(out), _ptr(offs), _ptr(workspace), _stream(x)))
+    return out, offs
+
+
+def decompress_pooled(buf: torch.Tensor, offs: torch.Tensor, dim: int, eb: torch.Tensor,
+                      y: Optional[torch.Tensor] = None, err_count: Optional[torch.Tensor] = None,
+                      in_bytes: Optional[int] = None) -> torch.Tensor:
+    """Inverse of compress_pooled: records in buf (in_bytes of them, default
+    the whole buffer) at offs ([n + 1] int64, device) -> y [n, d] float32.
+    Malformed records decode as zeros and add 1 each to err_count."""
+    _dev("buf", buf, torch.uint8)
+    _dev("offs", offs, torch.int64)
+    _dev("eb", eb, torch.float32)
+    n = offs.numel() - 1
+    if y is None:
+        y = torch.empty((max(n, 0), dim), dtype=torch.float32, device=buf.device)
+    _dev("y", y, torch.float32)
+    if y.numel() != max(n, 0) * dim:
+        raise ValueError("y must hold %d x %d values" % (n, dim))
+    nb = buf.numel() if in_bytes is None else int(in_bytes)
+    if nb > buf.numel():
+        raise ValueError("in_bytes exceeds the buffer")
+    _check("qemb_decompress_pooled", load_library().qemb_decompress_pooled(
+        _ptr(buf), nb, _ptr(offs), n, dim, eb.numel(), _ptr(eb), _ptr(y), _ptr(err_count), _stream(buf)))
+    return y

@@ -195,3 +195,45 @@ def test_binding_checks_the_packed_row_width(lib):
         qemb._check_rows(torch.zeros((10, 80), dtype=torch.uint8), 80, 11)
     with pytest.raises(ValueError):
         qemb._check_rows(torch.zeros(800, dtype=torch.uint8), 80, 10)
+
+
+def test_compress_sizes_and_argument_errors(lib):
+    for d in (1, 7, 64, 128, 1000, 1024):
+        for w in list(range(0, 33)):
+            assert lib.qemb_compress_record_bytes(d, w) == oracle.record_bytes(d, w)
+        assert lib.qemb_compress_bound(1000, d) == oracle.compress_bound(1000, d)
+    assert lib.qemb_compress_record_bytes(0, 4) == -1 and lib.qemb_compress_record_bytes(16, 33) == -1
+    assert lib.qemb_compress_record_bytes(1025, 4) == -1 and lib.qemb_compress_bound(-1, 16) == -1
+    assert lib.qemb_compress_workspace_bytes(0) == 0
+    assert lib.qemb_compress_workspace_bytes(1000) >= 8 * 16 + 1000
+    mis4 = ctypes.c_void_p((1 << 20) + 2)   # not 4-byte aligned
+    mis8 = ctypes.c_void_p((1 << 20) + 4)   # 4- but not 8-byte aligned
+    f = lib.qemb_compress_pooled
+    #        x     n    d   T  eb    out   offs  ws    stream
+    assert f(FAKE, -1, 16, 1, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 10, 0, 1, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 0, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 10, 2048, 1, FAKE, FAKE, FAKE, FAKE, None) == -3
+    assert f(None, 10, 16, 1, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 1, None, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 1, FAKE, None, FAKE, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 1, FAKE, FAKE, None, FAKE, None) == -1
+    assert f(FAKE, 10, 16, 1, FAKE, FAKE, FAKE, None, None) == -1
+    assert f(MIS, 10, 16, 1, FAKE, FAKE, FAKE, FAKE, None) == -2
+    assert f(FAKE, 10, 16, 1, FAKE, mis4, FAKE, FAKE, None) == -2
+    assert f(FAKE, 10, 16, 1, FAKE, FAKE, mis8, FAKE, None) == -2
+    assert f(FAKE, 10, 16, 1, FAKE, FAKE, FAKE, MIS, None) == -2
+    g = lib.qemb_decompress_pooled
+    #        in    bytes offs  n   d   T  eb    y     err   stream
+    assert g(FAKE, 100, FAKE, -1, 16, 1, FAKE, FAKE, None, None) == -1
+    assert g(FAKE, -1, FAKE, 10, 16, 1, FAKE, FAKE, None, None) == -1
+    assert g(FAKE, 100, FAKE, 10, 16, 0, FAKE, FAKE, None, None) == -1
+    assert g(FAKE, 100, FAKE, 10, 2048, 1, FAKE, FAKE, None, None) == -3
+    assert g(FAKE, 100, None, 10, 16, 1, FAKE, FAKE, None, None) == -1
+    assert g(FAKE, 100, FAKE, 10, 16, 1, None, FAKE, None, None) == -1
+    assert g(FAKE, 100, FAKE, 10, 16, 1, FAKE, None, None, None) == -1
+    assert g(None, 100, FAKE, 10, 16, 1, FAKE, FAKE, None, None) == -1
+    assert g(mis4, 100, FAKE, 10, 16, 1, FAKE, FAKE, None, None) == -2
+    assert g(FAKE, 100, mis8, 10, 16, 1, FAKE, FAKE, None, None) == -2
+    assert g(FAKE, 100, FAKE, 10, 16, 1, FAKE, MIS, None, None) == -2
+    assert g(None, 0, None, 0, 16, 1, None, None, None, None) == 0
