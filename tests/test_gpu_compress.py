@@ -92,6 +92,18 @@ def test_bounds_that_force_verbatim(q):
     assert np.all(w.reshape(-1, T)[:, :5] == oracle.RAW_WIDTH)
 
 
+def test_code_limit(q):
+    """|q| < 2^30: q = -(2^30 - 64) is coded in 31 bits, q = -2^30 and
+    +2^30 are stored verbatim (eb = 1, step 2, x = 2q exactly)."""
+    lim = np.zeros((4, 32), np.float32)
+    lim[0, 0] = np.float32(-(2.0 ** 31 - 128))
+    lim[1, 0] = np.float32(-(2.0 ** 31))
+    lim[2, 5] = np.float32(2.0 ** 31 - 128)
+    lim[3, 31] = np.float32(2.0 ** 31)
+    w = _compare(q, lim, 1, np.array([1.0], np.float32), "code limit")
+    assert list(w) == [31, oracle.RAW_WIDTH, 31, oracle.RAW_WIDTH]
+
+
 def test_adaptive_bounds_and_determinism(q):
     """The bound changes between calls (a looser one early in training, a
     tighter one later): each call matches the oracle under its own bounds,

@@ -148,6 +148,14 @@ def test_verbatim_cases():
     # eb = 1: 0.75 -> q = rint(0.375) = 0, |0.75 - 0| <= 1
     buf, offs, widths = oracle.compress_pooled(x, np.array([1.0], np.float32))
     assert widths[5] == 0 and widths[4] == 0
+    # the code limit |q| < 2^30: q = -(2^30 - 64) (the largest float below the
+    # limit) is coded in 31 bits, q = -2^30 is not (step 2: x = 2q exactly)
+    lim = np.zeros((2, 32), np.float32)
+    lim[0, 0] = np.float32(-(2.0 ** 31 - 128))
+    lim[1, 0] = np.float32(-(2.0 ** 31))
+    buf, offs, widths = oracle.compress_pooled(lim, np.array([1.0], np.float32))
+    assert list(widths) == [31, oracle.RAW_WIDTH]
+    assert list(np.diff(offs)) == [4 + 4 * 31, 4 + 4 * 32]
 
 
 def test_constant_grid_compression_ratio():
