@@ -73,7 +73,7 @@ def test_compress_matches_oracle(q, d):
     assert (w == oracle.RAW_WIDTH).any() and (w < oracle.RAW_WIDTH).any()
 
 
-@pytest.mark.parametrize("n", [0, 1, 63, 64, 65, 128, 1000, 64 * 1024 + 3])
+@pytest.mark.parametrize("n", [0, 1, 63, 64, 65, 128, 1000, 64 * 1024 + 3, 64 * 4096 + 65])
 def test_compress_vector_counts(q, n):
     print("compress n=%d" % n, flush=True)
     g = np.random.default_rng(13100 + n)
