@@ -19,6 +19,12 @@
  *    Systems", review page, "Proposed method").
  *  - Normalized l2 quantization error ("Post-Training 4-bit Quantization on
  *    Embedding Tables", review page, "Proposed method").
+ *  - Codebook rows (16 fp32 levels from 1-D k-means, 4-bit codes) and the
+ *    quantizer baselines the same page compares against; the dot
+ *    interaction of the pooled vectors (DLRM page, "Proposed method"); the
+ *    error-bounded compression of the pooled vectors a table-sharded model
+ *    exchanges ("Avancées dans les recommandations en Deep Learning",
+ *    scisimple page).  Each is stated with its entry points below.
  *
  * Packed row layout (stride S bytes, S = 16 * ceil((C + 4) / 16),
  * C = ceil(dim * bits / 8)):
