@@ -83,6 +83,20 @@ def test_compress_vector_counts(q, n):
     _compare(q, x, T, ebs, "n=%d" % n)
 
 
+@pytest.mark.parametrize("d", [5, 64, 128, 300])
+def test_arbitrary_bit_patterns(q, d):
+    """Random float32 bit patterns (NaN payloads, infinities, denormals, every
+    exponent) mixed with tame vectors, random bounds: records bit-exact."""
+    g = np.random.default_rng(13700 + d)
+    n, T = 300, 7
+    x = g.integers(0, 2 ** 32, size=(n, d), dtype=np.uint64).astype(np.uint32).view(np.float32)
+    tame = g.random(n) < 0.6
+    x[tame] = (g.integers(-1000, 1001, size=(int(tame.sum()), d)) * 1e-3).astype(np.float32)
+    ebs = np.exp(g.uniform(np.log(1e-6), np.log(10.0), size=T)).astype(np.float32)
+    w = _compare(q, x, T, ebs, "bit patterns d=%d" % d)
+    assert (w == oracle.RAW_WIDTH).any() and (w < oracle.RAW_WIDTH).any()
+
+
 def test_bounds_that_force_verbatim(q):
     g = np.random.default_rng(13200)
     d, T = 64, 6
