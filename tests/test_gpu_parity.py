@@ -96,7 +96,7 @@ def test_greedy_on_ctr_and_quantizer_workload_shapes(q):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("dim", [1, 3, 16, 33, 64, 128, 1000])
+@pytest.mark.parametrize("dim", [1, 2, 3, 5, 8, 16, 31, 32, 33, 63, 64, 65, 100, 128, 1000])
 def test_dequantize_arbitrary_rows(q, dim, bits):
     """Random code bytes and random finite fp16 scale/bias (not produced by
     the quantizer) decode identically."""
