@@ -153,7 +153,12 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // multi-hot bags (8+ ids on average): one wave per bag
   const int64_t mean_len = (nnz + a.n_bags - 1) / a.n_bags;
-  if (bits == 2) return mean_len >= 8 && a.C <= 32 ? dispatch_stream_int2(a, st) : dispatch_bag_int2(a, st);
+  if (bits == 2) {
+    if (mean_len >= 8) return a.C <= 32 ? dispatch_stream_int2(a, st) : dispatch_bag_int2(a, st);
+    // short bags: several bags per wave, 4-byte code chunks (16 codes) per lane
+    return dispatch_slice<2, 4>(a, next_pow2((a.C + 3) / 4), next_pow2((mean_len + kBagUnroll - 1) / kBagUnroll),
+                                st);
+  }
   if (mean_len >= 8) return bits == 4 ? dispatch_wave<4>(a, st) : dispatch_wave<8>(a, st);
   // short bags: several bags per wave; 8-byte code chunks per lane (16-byte
   // for INT8 rows wider than 512 codes), about kBagUnroll rows per group

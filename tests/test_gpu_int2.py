@@ -99,6 +99,22 @@ def test_int2_bag_short(q, dim):
     assert_pooled_close(got, ref, absd, "int2 short dim %d" % dim)
 
 
+@pytest.mark.parametrize("wid", [2, 3])
+def test_int2_one_hot_ctr_shapes(q, wid):
+    """The one-hot CTR workloads' shapes (one Zipf id per bag, sum pooling,
+    int32 ids) over 2-bit rows, tables scaled down: several bags per wave."""
+    w = synth.scaled(synth.workload(wid), rows=tuple(min(r, 5000) for r in synth.workload(wid).rows),
+                     batch=300)
+    x = np.concatenate([synth.table_values_np(w, t, 0, w.rows[t]) for t in range(w.n_tables)])
+    packed = oracle.quantize_rowwise(x, 2)
+    bt = synth.batch(w, index_dtype=np.int32)
+    got = host(q.bag_forward(dev(packed), dev(bt.table_offsets), bt.B, w.dim, 2, dev(bt.indices),
+                             dev(bt.offsets)))
+    ref, absd, err = oracle.bag_forward(packed, bt.table_offsets, bt.B, w.dim, 2, bt.indices, bt.offsets)
+    assert err == 0
+    assert_pooled_close(got, ref, absd, "int2 one-hot workload %d" % wid)
+
+
 def test_int2_bag_invalid_and_multi_hot(q):
     import torch
     g = np.random.default_rng(11300)
