@@ -248,13 +248,22 @@ int qemb_bag_forward_codebook(const uint8_t* packed, int64_t total_rows,
   const int64_t S = qemb_codebook_row_stride(dim);
   const int np = (dim + 127) / 128;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // short bags (fewer than 8 ids on average): four bags per wave
+  const bool short_bags = (nnz + n_bags - 1) / n_bags < 8;
   auto go = [&](auto idx_tag, auto np_tag) {
     using IdxT = decltype(idx_tag);
     constexpr int NP = decltype(np_tag)::value;
     constexpr int U = NP == 1 ? 8 : NP == 2 ? 4 : NP == 4 ? 4 : 2;
-    hipLaunchKernelGGL((bag_codebook_kernel<IdxT, NP, U>), dim3((unsigned)blocks), dim3(kBlock), 0,
-                       st, packed, S, total_rows, table_offsets, T, B, dim, indices, offsets, nnz,
-                       w, out, err_count, n_bags);
+    if (short_bags) {
+      hipLaunchKernelGGL((bag_codebook_short_kernel<IdxT, NP>),
+                         dim3((unsigned)((n_bags + kBlock / kCbLevels - 1) / (kBlock / kCbLevels))), dim3(kBlock),
+                         0, st, packed, S, total_rows, table_offsets, T, B, dim, indices, offsets, nnz, w, out,
+                         err_count, n_bags);
+    } else {
+      hipLaunchKernelGGL((bag_codebook_kernel<IdxT, NP, U>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                         st, packed, S, total_rows, table_offsets, T, B, dim, indices, offsets, nnz,
+                         w, out, err_count, n_bags);
+    }
     return launched();
   };
   auto by_np = [&](auto idx_tag) {

@@ -119,16 +119,17 @@ def _ragged(g, rows, B, max_len, dim, weighted):
                        np.concatenate([[0], np.cumsum(rows)]).astype(np.int64), B, T), lengths
 
 
+@pytest.mark.parametrize("max_len", [70, 6])  # multi-hot (one wave per bag) and short bags (four per wave)
 @pytest.mark.parametrize("dim", [1, 3, 16, 33, 64, 100, 128, 130, 256, 300, 513, 1000, 1024])
 @pytest.mark.parametrize("weighted", [False, True])
-def test_bag_codebook_dims_ragged_bags(q, dim, weighted):
-    print("codebook bag dim=%d weighted=%d" % (dim, weighted), flush=True)
-    g = np.random.default_rng(7500 + dim * 3 + weighted)
+def test_bag_codebook_dims_ragged_bags(q, dim, weighted, max_len):
+    print("codebook bag dim=%d weighted=%d max_len=%d" % (dim, weighted, max_len), flush=True)
+    g = np.random.default_rng(7500 + dim * 3 + weighted + max_len)
     rows = [1, 57, 300]
     x = special_rows(g, sum(rows), dim)
     x[np.abs(x) > 100] = 1.0  # keep the tolerance meaningful
     packed = oracle.quantize_codebook(x)
-    bt, lengths = _ragged(g, rows, 97, 70, dim, weighted)
+    bt, lengths = _ragged(g, rows, 97, max_len, dim, weighted)
     got, err, ref, absd, rerr = _run(q, packed, bt, dim, bt.weights)
     assert err == rerr == 0
     assert_pooled_close(got, ref, absd, "codebook dim %d" % dim)
@@ -166,14 +167,15 @@ def test_bag_codebook_long_bags(q):
     assert_pooled_close(got, ref, absd, "codebook long bags")
 
 
-def test_bag_codebook_invalid_ids_offsets_and_tables(q):
-    g = np.random.default_rng(7700)
+@pytest.mark.parametrize("max_len", [11, 90])  # short bags (four per wave) and multi-hot bags
+def test_bag_codebook_invalid_ids_offsets_and_tables(q, max_len):
+    g = np.random.default_rng(7700 + max_len)
     dim, T, B = 64, 4, 50
     rows = [100, 10, 1, 40]
     x = special_rows(g, sum(rows), dim)
     x[np.abs(x) > 100] = 1.0
     packed = oracle.quantize_codebook(x)
-    lengths = g.integers(0, 12, size=T * B)
+    lengths = g.integers(0, max_len + 1, size=T * B)
     offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
     idx = np.concatenate([g.integers(-5, rows[gb // B] + 5, size=lengths[gb])
                           for gb in range(T * B)]).astype(np.int64)
@@ -195,6 +197,20 @@ def test_bag_codebook_invalid_ids_offsets_and_tables(q):
     got, err, ref, absd, rerr = _run(q, packed, bt2, dim, bt.weights)
     assert err == rerr
     assert_pooled_close(got, ref, absd, "codebook empty table")
+
+
+@pytest.mark.parametrize("wid", [2, 3])
+def test_bag_codebook_one_hot_ctr_shapes(q, wid):
+    """The one-hot CTR workloads' shapes (one Zipf id per bag, sum pooling,
+    int32 ids) over codebook rows, tables scaled down: four bags per wave."""
+    w0 = synth.workload(wid)
+    w = synth.scaled(w0, rows=tuple(min(r, 3000) for r in w0.rows), batch=200)
+    x = np.concatenate([synth.table_values_np(w, t, 0, w.rows[t]) for t in range(w.n_tables)])
+    packed = oracle.quantize_codebook(x)
+    bt = synth.batch(w, index_dtype=np.int32)
+    got, err, ref, absd, rerr = _run(q, packed, bt, w.dim)
+    assert err == rerr == 0
+    assert_pooled_close(got, ref, absd, "codebook one-hot workload %d" % wid)
 
 
 def test_bag_codebook_no_rows_no_ids_single_bag(q):
