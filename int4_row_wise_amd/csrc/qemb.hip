@@ -43,7 +43,6 @@ constexpr int kBlock = 256;
 #include "l2_error.inc"
 #include "baselines.inc"
 #include "codebook.inc"
-#include "lookup_int2.inc"
 #include "interaction.inc"
 #include "compress.inc"
 #include "host.inc"
@@ -154,7 +153,7 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
   // multi-hot bags (8+ ids on average): one wave per bag
   const int64_t mean_len = (nnz + a.n_bags - 1) / a.n_bags;
   if (bits == 2) {
-    if (mean_len >= 8) return a.C <= 32 ? dispatch_stream_int2(a, st) : dispatch_bag_int2(a, st);
+    if (mean_len >= 8) return dispatch_wave<2>(a, st);  // stream kernel up to 8 lanes per row, then the wave kernel
     // short bags: several bags per wave, 4-byte code chunks (16 codes) per lane
     return dispatch_slice<2, 4>(a, next_pow2((a.C + 3) / 4), next_pow2((mean_len + kBagUnroll - 1) / kBagUnroll),
                                 st);
