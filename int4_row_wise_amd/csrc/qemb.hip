@@ -7,6 +7,8 @@
 //   * dequant_kernel          packed rows -> fp32
 //   * bag_stream_kernel       fused decode + (weighted) sum pooling of multi-hot
 //                             bags, pipelined over batches of ids
+//   * bag_pack_kernel         the same over runs of 64 bags whose ids are packed
+//                             into full batches (bags of a few to a few tens of ids)
 //   * bag_wave_kernel         the same for rows wider than 8 lanes
 //   * bag_slice_kernel        the same for short bags, several bags per wave
 //   * l2_partial/l2_final     normalized l2 error, fixed-order reduction
@@ -29,6 +31,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "qemb.h"
 
@@ -40,6 +43,7 @@ constexpr int kBlock = 256;
 #include "common.inc"
 #include "quantize.inc"
 #include "lookup.inc"
+#include "pack.inc"
 #include "l2_error.inc"
 #include "baselines.inc"
 #include "codebook.inc"
@@ -150,23 +154,36 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
   a.n_bags = (int64_t)T * B;
   a.vec4 = (dim % 4 == 0);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  // multi-hot bags (8+ ids on average): one wave per bag
+  // Kernel choice by row width (lanes of 16 codes per row) and mean bag
+  // length, from timings of the three bag kernels over bag-length mixes:
+  //   rows of 4..8 lanes, mean length up to 16 (24 for INT4): runs of 64
+  //     bags packed into full id batches;
+  //   rows of 1..2 lanes, mean length up to 16, and wider rows with bags of
+  //     under 8 ids: several bags per wave;
+  //   longer bags: one wave per bag (the stream kernel up to 8 lanes per
+  //     row, the wave kernel beyond).
   const int64_t mean_len = (nnz + a.n_bags - 1) / a.n_bags;
   if (bits == 2) {
-    if (mean_len >= 8) return dispatch_wave<2>(a, st);  // stream kernel up to 8 lanes per row, then the wave kernel
-    // short bags: several bags per wave, 4-byte code chunks (16 codes) per lane
+    const int lpr = pack_lanes<2>(a);
+    if (lpr >= 4 && mean_len <= 16) return dispatch_pack<2>(a, st);
+    if (mean_len > 16 || (lpr < 0 && mean_len >= 8)) return dispatch_wave<2>(a, st);
+    // several bags per wave, 4-byte code chunks (16 codes) per lane
     return dispatch_slice<2, 4>(a, next_pow2((a.C + 3) / 4), next_pow2((mean_len + kBagUnroll - 1) / kBagUnroll),
                                 st);
   }
-  if (mean_len >= 8) return bits == 4 ? dispatch_wave<4>(a, st) : dispatch_wave<8>(a, st);
-  // short bags: several bags per wave; 8-byte code chunks per lane (16-byte
-  // for INT8 rows wider than 512 codes), about kBagUnroll rows per group
+  const int lpr = bits == 4 ? pack_lanes<4>(a) : pack_lanes<8>(a);
+  if (lpr >= 4 && mean_len <= (bits == 4 ? 24 : 16))
+    return bits == 4 ? dispatch_pack<4>(a, st) : dispatch_pack<8>(a, st);
+  if (mean_len > 16 || (lpr < 0 && mean_len >= 8))
+    return bits == 4 ? dispatch_wave<4>(a, st) : dispatch_wave<8>(a, st);
+  // several bags per wave; 8-byte code chunks per lane (16-byte for INT8
+  // rows wider than 512 codes), about kBagUnroll rows per group
   const int64_t chunks8 = (a.C + 7) / 8;
   const int vec = chunks8 > 64 ? 16 : 8;
-  const int lpr = next_pow2((a.C + vec - 1) / vec);
+  const int slpr = next_pow2((a.C + vec - 1) / vec);
   const int rg = next_pow2((mean_len + kBagUnroll - 1) / kBagUnroll);
-  if (bits == 4) return dispatch_slice<4, 8>(a, lpr, rg, st);
-  if (vec == 8) return dispatch_slice<8, 8>(a, lpr, rg, st);
+  if (bits == 4) return dispatch_slice<4, 8>(a, slpr, rg, st);
+  if (vec == 8) return dispatch_slice<8, 8>(a, slpr, rg, st);
   return dispatch_slice_rg<8, 16, 64>(a, rg, st);  // only rows wider than 512 codes get here
 }
 

@@ -335,3 +335,65 @@ def test_tables_over_2gb_take_64bit_addressing(q):
     check_sampled_bags(q, w, cb, 4, None, bt, out, 300, 99, codebook=True)
     del cb
     torch.cuda.empty_cache()
+
+
+def _drop_ids(bt, keep):
+    """The batch with the ids where `keep` is False taken out of their bags."""
+    lens = np.diff(bt.offsets.astype(np.int64))
+    bag_of = np.repeat(np.arange(lens.size), lens)
+    new_lens = np.bincount(bag_of[keep], minlength=lens.size)
+    offs = np.concatenate([[0], np.cumsum(new_lens)]).astype(bt.offsets.dtype)
+    w = None if bt.weights is None else bt.weights[keep]
+    return synth.Batch(bt.indices[keep], offs, w, bt.table_offsets, bt.B, bt.T)
+
+
+def _shorten_bags(bt, max_len):
+    """Each bag cut to 1 + (len - 1) % max_len of its first ids."""
+    offs = bt.offsets.astype(np.int64)
+    lens = np.diff(offs)
+    cut = np.where(lens > 0, 1 + (lens - 1) % max_len, 0)
+    keep = np.zeros(bt.indices.size, bool)
+    for b in np.nonzero(cut)[0]:
+        keep[offs[b]:offs[b] + cut[b]] = True
+    return _drop_ids(bt, keep)
+
+
+def test_over_2gb_invalid_ids_and_nonfinite_first_row(q):
+    """A 2.24 GB table (28M INT4 rows of d=128: rows read with 64-bit
+    addresses) whose first row has an fp16 scale of +inf, and about 5% of the
+    ids outside their table.  On the 64-bit path a slot without a valid row
+    reads the table's first row; it must still add exactly 0.  Multi-hot
+    bags (one wave per bag) and bags of at most 8 ids (packed runs), int32
+    and int64 ids: error counts exact, and sampled bags against the oracle on
+    the same bags with the invalid ids taken out (an invalid id adds
+    nothing)."""
+    import torch
+    w = synth.scaled(synth.workload(4), rows=(28_000_000, 1000), batch=2000)
+    print("table over 2 GB, invalid ids, first row +inf", flush=True)
+    packed = pack_tables(q, w, 4, q.RANGE)
+    C = (w.dim * 4 + 7) // 8
+    packed[0, C:C + 2] = torch.tensor([0x00, 0x7C], dtype=torch.uint8, device="cuda")  # scale +inf
+    g = np.random.default_rng(4242)
+    long_bt = synth.batch(w, batch_seed=2, index_dtype=np.int64)
+    for name, bt in (("multi-hot", long_bt), ("short", _shorten_bags(long_bt, 8))):
+        offs = bt.offsets.astype(np.int64)
+        table = np.repeat(np.arange(bt.T), [offs[(t + 1) * bt.B] - offs[t * bt.B] for t in range(bt.T)])
+        ids = bt.indices.astype(np.int64).copy()
+        ids[(table == 0) & (ids == 0)] = 1  # no valid id of the first row
+        bad = g.random(ids.size) < 0.05
+        nt = np.array(w.rows, np.int64)[table]
+        ids[bad] = np.choose(g.integers(0, 4, size=ids.size), [
+            np.full(ids.size, -1), nt, nt + 12345, np.full(ids.size, -(1 << 31))])[bad]
+        bt = synth.Batch(ids, bt.offsets, bt.weights, bt.table_offsets, bt.B, bt.T)
+        n_bad = int(bad.sum())
+        assert n_bad > 100
+        for itype in (np.int32, np.int64):
+            print("  %s bags, %s ids" % (name, itype.__name__), flush=True)
+            err = torch.zeros(1, dtype=torch.int32, device="cuda")
+            out = host(q.bag_forward(packed, dev(bt.table_offsets), bt.B, w.dim, 4, dev(ids.astype(itype)),
+                                     dev(bt.offsets.astype(itype)), dev(bt.weights), err_count=err))
+            assert int(host(err)[0]) == n_bad
+            assert np.isfinite(out).all()
+            check_sampled_bags(q, w, packed, 4, oracle.RANGE, _drop_ids(bt, ~bad), out, 300, 77)
+    del packed
+    torch.cuda.empty_cache()
