@@ -33,9 +33,14 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
-VALU_PEAK_OPS = 256 * 64 * 2.4e9  # lane-ops/s: 256 CUs x 64 lanes x 2.4 GHz (no packed fp32)
+# fp32 VALU issue peak in lane-instructions/s: 256 CUs x 128 lanes x 2.4 GHz
+# (the published 157.3 TFLOP/s fp32 vector peak counts an FMA as 2 flops;
+# the counters show more than one wave64 VALU instruction per CU per cycle,
+# so the 128 lanes per CU per clock are two wave64 instructions)
+VALU_PEAK_LANE_INSTS = 256 * 128 * 2.4e9
 HEADLINE_KERNEL = "bag_stream_kernel<4, 8, int, true, true, true>"
 COUNTERS = os.path.join(ROOT, "profiles", "bag_stream_int4_multihot_counters.md")
+QUANT_COUNTERS = os.path.join(ROOT, "profiles", "quantizer_workload_counters.md")
 
 
 def log(msg: str) -> None:
@@ -56,6 +61,8 @@ def parse():
                     help="error-bounded compression of the pooled output only")
     ap.add_argument("--interaction-only", action="store_true",
                     help="only one INT4 lookup and the dot interaction on its output (for profiling)")
+    ap.add_argument("--quantizer-only", action="store_true",
+                    help="only the quantizer workload (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -79,13 +86,11 @@ def algorithmic_codebook_bytes(nnz: int, n_bags: int, dim: int, idx_bytes: int,
     return nnz * per + (n_bags + 1) * idx_bytes + n_bags * dim * 4
 
 
-def measured_traffic():
-    """HBM bytes per launch of the headline kernel from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
-    counter reads for a plain device copy of known size), or None when the
+def counter_record(path):
+    """The json block of a committed counter summary, or None when the
     summary is missing or was taken on a different kernel source."""
     try:
-        text = open(COUNTERS).read()
+        text = open(path).read()
     except OSError:
         return None
     start = text.find("```json")
@@ -96,6 +101,16 @@ def measured_traffic():
     from int4_row_wise_amd import build as qbuild
     src = qbuild.source_sha256()
     if rec.get("source_sha256") != src or qbuild.built_source_sha256() != src:
+        return None
+    return rec
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the
+    counter reads for a plain device copy of known size), or None."""
+    rec = counter_record(COUNTERS)
+    if rec is None:
         return None
     return 1024.0 * (rec["fetch_kib_per_dispatch"] * rec["fetch_scale"] +
                      rec["write_kib_per_dispatch"] * rec["write_scale"])
@@ -265,10 +280,11 @@ def bench_cold(q, torch, packed, toff, batch, w, bits, out, dev, reps=5):
     return ms
 
 
-def quantizer_extras(q, synth, torch, dev, reps=3):
+def quantizer_extras(q, synth, torch, dev, oracle=None, reps=3):
     """The quantizer workload: one 5e7 x 64 table (99% N(0,0.02) / 1%
     Laplace(0,0.2)), range and greedy INT4 quantization (200 bins, 100
-    steps), full-table dequantize, normalized l2 of both encodings."""
+    steps), full-table dequantize, normalized l2 of both encodings; with
+    `oracle`, the oracle's rows/s for the same operations on a row prefix."""
     w = synth.workload(5)
     rows, dim = w.rows[0], w.dim
     x = synth.table_values_torch(w, 0, 0, rows, dev)
@@ -296,14 +312,24 @@ def quantizer_extras(q, synth, torch, dev, reps=3):
     res["dequantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3, "GBps": (in_b + out_b) / ms / 1e6,
                          "hbm_frac": (in_b + out_b) / ms / 1e6 / HBM_PEAK_GBS}
     ms = timed(lambda: q.quantize_rowwise(x, 4, q.GREEDY, w.n_bins, w.n_steps, out=packed), 1)
-    # algorithmic lane-ops: 2K+1 candidate windows per row, each 8 fp32
-    # operations per element (x - b, * 1/s, round, clamp, s*q + b, x - y,
-    # square, pairwise add); the per-window setup (two divisions, fp16
-    # round trips) is not counted
-    ops = rows * (2 * w.n_steps + 1) * (8 * dim)
     res["greedy_quantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3,
-                              "valu_ops_per_s": ops / ms * 1e3,
-                              "valu_frac": ops / ms * 1e3 / VALU_PEAK_OPS}
+                              "windows_per_row": 2 * w.n_steps + 1}
+    # VALU issue rate: the kernel's wave64 VALU instructions per launch as
+    # counted by SQ_INSTS_VALU on this source (committed summary), over this
+    # run's launch time, against 128 lanes per CU per clock
+    rec = counter_record(QUANT_COUNTERS)
+    if rec is not None and rec["rows"] == rows and rec["dim"] == dim and \
+            rec["windows_per_row"] == 2 * w.n_steps + 1:
+        lane_insts = rec["valu_insts_per_dispatch"] * 64
+        cycles = rec["grbm_gui_active_per_dispatch"] / rec["xcds"]
+        res["greedy_quantize"].update({
+            "bound": "alu", "valu_lane_insts_per_launch": lane_insts,
+            "lane_insts_per_element_window": lane_insts / (rows * dim * (2 * w.n_steps + 1)),
+            "valu_lane_insts_per_s": lane_insts / ms * 1e3,
+            "valu_frac": lane_insts / ms * 1e3 / VALU_PEAK_LANE_INSTS,
+            "valu_peak_lane_insts_per_s": VALU_PEAK_LANE_INSTS,
+            "counted_insts_per_cu_cycle": rec["valu_insts_per_dispatch"] / (256 * cycles),
+            "counted_clock_ghz": cycles / (rec["traced_avg_us"] * 1e-6) / 1e9})
     res["greedy_l2"] = q.l2_error(x, packed, 4)
     del packed
     cb = torch.empty((rows, q.codebook_row_stride(dim)), dtype=torch.uint8, device=dev)
@@ -340,6 +366,20 @@ def quantizer_extras(q, synth, torch, dev, reps=3):
     res["codebook_dequantize"] = {"ms": ms, "rows_per_s": rows / ms * 1e3,
                                   "GBps": (in_b + cb_out) / ms / 1e6,
                                   "hbm_frac": (in_b + cb_out) / ms / 1e6 / HBM_PEAK_GBS}
+    if oracle is not None:
+        x_np = x[: 1 << 20].cpu().numpy()
+        rr = oracle_quantizer_rates(oracle, x_np, 4, oracle.RANGE, w.n_bins, w.n_steps, 1 << 20, 1 << 16)
+        rg = oracle_quantizer_rates(oracle, x_np, 4, oracle.GREEDY, w.n_bins, w.n_steps, 1 << 16, 1 << 12)
+        res["cpu_oracle"] = {
+            "kind": "oracle", "cores": rr["quantize"]["cores"],
+            "range_rows_per_s": rr["quantize"]["per_s"],
+            "range_rows_per_s_one_thread": rr["quantize"]["one_thread_per_s"],
+            "greedy_rows_per_s": rg["quantize"]["per_s"],
+            "greedy_rows_per_s_one_thread": rg["quantize"]["one_thread_per_s"],
+            "dequantize_rows_per_s": rr["dequantize"]["per_s"],
+            "dequantize_rows_per_s_one_thread": rr["dequantize"]["one_thread_per_s"],
+            "sample": "first 2^20 rows (range, dequantize; one thread 2^16) and 2^16 rows (greedy; "
+                      "one thread 2^12) of the table"}
     del x, y, cb
     torch.cuda.empty_cache()
     return res
@@ -449,6 +489,141 @@ def compress_extras(q, torch, pooled, dev, steps=20, warmup=3):
             "compress_bytes_per_call": bc, "decompress_bytes_per_call": bd}
 
 
+def oracle_rate(oracle, fn, n_all: int, n_one: int, budget_s: float = 4.0):
+    """Units/s of the oracle running fn(n) over the first n units: all of the
+    oracle's threads on n_all units (repeated within budget_s), and one
+    thread on n_one units."""
+    threads = oracle.num_threads()
+    reps, t_all = 0, 0.0
+    while reps == 0 or (t_all < budget_s and reps < 20):
+        t0 = time.perf_counter()
+        fn(n_all)
+        t_all += time.perf_counter() - t0
+        reps += 1
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        fn(n_one)
+        t_one = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(threads)
+    return {"per_s": n_all * reps / t_all, "cores": threads, "sample": n_all, "reps": reps,
+            "one_thread_per_s": n_one / t_one, "one_thread_sample": n_one}
+
+
+def oracle_quantizer_rates(oracle, x_np, bits, mode, n_bins, n_steps, n_all, n_one):
+    """Oracle rows/s for quantize (mode) and dequantize over a row prefix."""
+    def quant(n):
+        oracle.quantize_rowwise(x_np[:n], bits, mode, n_bins, n_steps)
+    packed = oracle.quantize_rowwise(x_np[:max(n_all, n_one)], bits, mode, n_bins, n_steps)
+    dim = x_np.shape[1]
+
+    def deq(n):
+        oracle.dequantize(packed[:n], dim, bits)
+    return {"quantize": oracle_rate(oracle, quant, n_all, n_one),
+            "dequantize": oracle_rate(oracle, deq, min(n_all * 4, packed.shape[0]), n_one)}
+
+
+def ctr_extras(q, synth, torch, oracle, dev, wid, steps=50, warmup=5, with_oracle=True):
+    """A one-hot workload end to end: every table drawn on the GPU and
+    quantized by the library (timed per chunk of at most 2^24 rows; HIP
+    events), then the one-hot pooled lookup of one batch (timed per launch),
+    and the oracle on the same operations: quantize of a row prefix of the
+    largest table, the lookup of the whole batch over oracle-packed copies
+    of the rows it references."""
+    w = synth.workload(wid)
+    bits = 4
+    mode = q.GREEDY if w.clip == "greedy" else q.RANGE
+    S = q.row_stride(w.dim, bits)
+    C = (w.dim * bits + 7) // 8
+    packed = torch.empty((w.total_rows, S), dtype=torch.uint8, device=dev)
+    tm = Timer(torch)
+    r0 = 0
+    for t in range(w.n_tables):
+        n = w.rows[t]
+        for c0 in range(0, n, 1 << 24):
+            m = min(1 << 24, n - c0)
+            x = synth.table_values_torch(w, t, c0, m, dev)
+            if mode == q.GREEDY:
+                fn = lambda: q.quantize_rowwise(x, bits, mode, w.n_bins, w.n_steps, out=packed[r0 + c0:r0 + c0 + m])
+            else:
+                fn = lambda: q.quantize_rowwise(x, bits, mode, out=packed[r0 + c0:r0 + c0 + m])
+            with tm:
+                fn()
+            del x
+        r0 += n
+    qms = float(np.sum(tm.ms()))
+    qbytes = w.total_rows * (w.dim * 4 + C + 4)
+    res = {"workload": w.name, "rows": w.total_rows, "tables": w.n_tables, "dim": w.dim,
+           "quantize": {"clip": w.clip, "ms_all_tables": qms, "rows_per_s": w.total_rows / qms * 1e3,
+                        "GBps": qbytes / qms / 1e6, "hbm_frac": qbytes / qms / 1e6 / HBM_PEAK_GBS}}
+    bt = synth.batch(w, batch_seed=0, index_dtype=np.int32)
+    toff = to_dev(torch, bt.table_offsets, dev)
+    idx, offs = to_dev(torch, bt.indices, dev), to_dev(torch, bt.offsets, dev)
+    out = torch.empty((bt.B, bt.T, w.dim), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        q.bag_forward(packed, toff, bt.B, w.dim, bits, idx, offs, out=out)
+    torch.cuda.synchronize()
+    tl = Timer(torch)
+    for _ in range(steps):
+        with tl:
+            q.bag_forward(packed, toff, bt.B, w.dim, bits, idx, offs, out=out)
+    ms = tl.ms()
+    n_bags = bt.T * bt.B
+    lb = algorithmic_bag_bytes(bt.nnz, n_bags, w.dim, bits, 4, False)
+    res["lookup"] = {"batch": bt.B, "lookups": bt.nnz, "launch_ms": launch_stats(ms),
+                     "lookups_per_s": bt.nnz / (np.mean(ms) * 1e-3),
+                     "GBps": lb / (np.mean(ms) * 1e-3) / 1e9,
+                     "hbm_frac": lb / (np.mean(ms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "bytes_per_launch": lb}
+    del packed
+    torch.cuda.empty_cache()
+    if not with_oracle:
+        return res
+    omode = oracle.GREEDY if w.clip == "greedy" else oracle.RANGE
+    big = int(np.argmax(w.rows))
+    n_pre = min(w.rows[big], 1 << 20 if omode == oracle.RANGE else 1 << 16)
+    x_np = synth.table_values_torch(w, big, 0, n_pre, dev).cpu().numpy()
+    rates = oracle_quantizer_rates(oracle, x_np, bits, omode, w.n_bins, w.n_steps, n_pre,
+                                   max(1, n_pre // 16))
+    # the lookup: oracle-packed copies of the referenced rows, ids remapped
+    idx64 = bt.indices.astype(np.int64)
+    mini, sub = [], np.empty_like(idx64)
+    base = 0
+    for t in range(bt.T):
+        sl = slice(bt.offsets[t * bt.B], bt.offsets[(t + 1) * bt.B])
+        u, inv = np.unique(idx64[sl], return_inverse=True)
+        xr = torch.empty((u.size, w.dim), dtype=torch.float32)
+        for c in np.unique(u // synth.CHUNK_ROWS):
+            sel = np.nonzero(u // synth.CHUNK_ROWS == c)[0]
+            r0c = int(c) * synth.CHUNK_ROWS
+            blk = synth.table_values_torch(w, t, r0c, min(synth.CHUNK_ROWS, w.rows[t] - r0c), dev)
+            xr[torch.from_numpy(sel)] = blk[torch.from_numpy(u[sel] - r0c).to(dev)].cpu()
+            del blk
+        mini.append(oracle.quantize_rowwise(xr.numpy(), bits, omode, w.n_bins, w.n_steps))
+        sub[sl] = inv + base
+        base += u.size
+    mp = np.concatenate(mini)
+    mtoff = np.array([0, mp.shape[0]], np.int64)
+    n_bag = bt.T * bt.B
+
+    def look(nb):
+        oracle.bag_forward(mp, mtoff, nb, w.dim, bits, sub[:bt.offsets[nb]], bt.offsets[:nb + 1])
+    lr = oracle_rate(oracle, look, n_bag, max(1, n_bag // 16))
+    res["cpu_oracle"] = {
+        "kind": "oracle", "cores": rates["quantize"]["cores"],
+        "quantize_rows_per_s": rates["quantize"]["per_s"],
+        "quantize_rows_per_s_one_thread": rates["quantize"]["one_thread_per_s"],
+        "quantize_sample": "first %d rows of table %d (one thread: first %d)" % (
+            n_pre, big, rates["quantize"]["one_thread_sample"]),
+        "dequantize_rows_per_s": rates["dequantize"]["per_s"],
+        "dequantize_rows_per_s_one_thread": rates["dequantize"]["one_thread_per_s"],
+        "lookups_per_s": lr["per_s"] * (bt.nnz / n_bag),
+        "lookups_per_s_one_thread": lr["one_thread_per_s"] * (bt.nnz / n_bag),
+        "lookup_sample": "the whole batch (%d bags) over oracle-packed copies of its rows" % n_bag}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -471,10 +646,11 @@ def main():
     from int4_row_wise_amd import build as qbuild
     from int4_row_wise_amd import synth
     qbuild.ensure_built()
-    if qbuild.built_source_sha256() != qbuild.source_sha256():
-        log("warning: libqemb.so was not built from the current kernel source")
-    q.load_library()
+    q.load_library()  # raises unless the library was built from the current kernel sources
     dev = torch.device("cuda:0")
+    if args.quantizer_only:
+        print(json.dumps({"quantizer": quantizer_extras(q, synth, torch, dev)}), flush=True)
+        return
     w = synth.workload(4)
     bits_list = (4,) if (args.no_extras or args.interaction_only or args.compress_only) else (4, 8)
 
@@ -595,8 +771,16 @@ def main():
         torch.cuda.empty_cache()
         result["codebook"] = codebook_extras(q, synth, torch, w, toff, batches, out, dev, n_bags)
         t0 = time.time()
-        result["quantizer"] = quantizer_extras(q, synth, torch, dev)
+        oracle_mod = None
+        if not args.no_cpu_baseline:
+            import oracle as oracle_mod
+        result["quantizer"] = quantizer_extras(q, synth, torch, dev, oracle_mod)
         log("quantizer workload done in %.1fs" % (time.time() - t0))
+        for wid, key in ((1, "tiny"), (2, "ctr_one_hot"), (3, "large_ctr_one_hot")):
+            t0 = time.time()
+            result[key] = ctr_extras(q, synth, torch, oracle_mod, dev, wid,
+                                     with_oracle=oracle_mod is not None)
+            log("%s workload done in %.1fs" % (key, time.time() - t0))
 
     if not args.no_cpu_baseline:
         import oracle

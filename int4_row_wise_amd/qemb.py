@@ -48,6 +48,23 @@ class QembError(RuntimeError):
 _lib = None
 
 
+def check_built_from_current_source(path: str = LIB_PATH) -> None:
+    """Raise unless the library at `path` records (in `path`.srchash, written
+    by the build) the hash of the kernel sources now in the package: a
+    library left from older sources must not run in their place."""
+    from int4_row_wise_amd import build as qbuild
+    try:
+        with open(path + ".srchash") as f:
+            built = f.read().strip()
+    except OSError:
+        built = None
+    now = qbuild.source_sha256()
+    if built != now:
+        raise QembError("load_library", -101,
+                        "%s was built from other kernel sources (recorded %s, sources now %s); "
+                        "rebuild with `python -m int4_row_wise_amd.build`" % (path, built, now))
+
+
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
@@ -55,6 +72,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise QembError("load_library", -100,
                         "%s is not built (run `python -m int4_row_wise_amd.build`)" % path)
+    check_built_from_current_source(path)
     L = ctypes.CDLL(path)
     p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     L.qemb_abi_version.restype = ctypes.c_int

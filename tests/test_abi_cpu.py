@@ -237,3 +237,22 @@ def test_compress_sizes_and_argument_errors(lib):
     assert g(FAKE, 100, mis8, 10, 16, 1, FAKE, FAKE, None, None) == -2
     assert g(FAKE, 100, FAKE, 10, 16, 1, FAKE, MIS, None, None) == -2
     assert g(None, 0, None, 0, 16, 1, None, None, None, None) == 0
+
+
+def test_library_from_other_sources_is_refused(tmp_path, lib):
+    """A library whose recorded source hash differs from the kernel sources
+    now in the package (left from an older build) is refused before it is
+    loaded; the current build is accepted."""
+    import shutil
+
+    from int4_row_wise_amd import qemb
+    qemb.check_built_from_current_source(qbuild.LIB)
+    stale = tmp_path / "libqemb.so"
+    shutil.copy(qbuild.LIB, stale)
+    with open(str(stale) + ".srchash", "w") as f:
+        f.write("0" * 64 + "\n")
+    with pytest.raises(qemb.QembError, match="other kernel sources"):
+        qemb.check_built_from_current_source(str(stale))
+    os.remove(str(stale) + ".srchash")
+    with pytest.raises(qemb.QembError, match="other kernel sources"):
+        qemb.check_built_from_current_source(str(stale))

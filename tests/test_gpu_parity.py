@@ -341,3 +341,11 @@ def test_bag_on_gpu_packed_table(q):
         ref, absd, _ = oracle.bag_forward(ref_packed, bt.table_offsets, bt.B, w.dim, bits,
                                           bt.indices, bt.offsets, bt.weights)
         assert_pooled_close(host(out), ref, absd, "gpu-packed %d" % bits)
+
+
+def test_loaded_library_is_built_from_current_sources(q):
+    """The library the GPU tests run was built from the kernel sources in
+    this tree (a stale build is refused at load time)."""
+    from int4_row_wise_amd import build as qbuild
+    q.qemb.check_built_from_current_source(qbuild.LIB)
+    assert qbuild.built_source_sha256() == qbuild.source_sha256()
