@@ -397,3 +397,42 @@ def test_over_2gb_invalid_ids_and_nonfinite_first_row(q):
             check_sampled_bags(q, w, packed, 4, oracle.RANGE, _drop_ids(bt, ~bad), out, 300, 77)
     del packed
     torch.cuda.empty_cache()
+
+
+def test_multi_hot_full_output_every_bag(q):
+    """The multi-hot workload at full size (64 tables x 1M rows, d=128,
+    batch 16384, U{1..64} bags, Zipf ids, weights), INT4: the whole table as
+    packed by the GPU quantizer equals the oracle's packing of the same
+    generated values byte for byte (64M rows), and every one of the 1M pooled
+    outputs of one batch is within tolerance of the oracle's, in the launch
+    configuration the benchmark times."""
+    import torch
+    w = synth.workload(4)
+    print("multi-hot full output: packing", flush=True)
+    S = q.row_stride(w.dim, 4)
+    packed = torch.empty((w.total_rows, S), dtype=torch.uint8, device="cuda")
+    ref_packed = np.empty((w.total_rows, S), dtype=np.uint8)
+    r0 = 0
+    for t in range(w.n_tables):
+        n = w.rows[t]
+        x = synth.table_values_torch(w, t, 0, n, "cuda")
+        q.quantize_rowwise(x, 4, q.RANGE, out=packed[r0:r0 + n])
+        ref_packed[r0:r0 + n] = oracle.quantize_rowwise(x.cpu().numpy(), 4, oracle.RANGE)
+        del x
+        r0 += n
+    gp = host(packed)
+    same = np.array_equal(gp, ref_packed)
+    assert same, "%d packed rows differ" % int((gp != ref_packed).any(1).sum())
+    del gp
+    bt = synth.batch(w, batch_seed=0, index_dtype=np.int32)
+    print("multi-hot full output: lookup of %d bags" % (bt.T * bt.B), flush=True)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = host(q.bag_forward(packed, dev(bt.table_offsets), bt.B, w.dim, 4, dev(bt.indices),
+                             dev(bt.offsets), dev(bt.weights), err_count=err))
+    del packed
+    torch.cuda.empty_cache()
+    ref, absd, rerr = oracle.bag_forward(ref_packed, bt.table_offsets, bt.B, w.dim, 4, bt.indices,
+                                         bt.offsets, bt.weights)
+    assert int(host(err)[0]) == rerr == 0
+    worst = assert_pooled_close(out, ref, absd, "every bag of the multi-hot batch")
+    print("worst |err| / tolerance: %.3g" % worst, flush=True)

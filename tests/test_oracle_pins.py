@@ -398,6 +398,49 @@ def test_oracle_matches_independent_numpy_model_bit_for_bit(oracle_lib):
     assert n_cases == 7 * 3 * 12 * 2
 
 
+def _tiny_row(g, d):
+    """A tiny row of one of the value kinds the rules single out."""
+    kind = int(g.integers(0, 9))
+    scale = float(g.choice([1e-7, 1e-3, 0.02, 1.0, 300.0, 20000.0]))
+    x = (g.standard_normal(d) * scale).astype(np.float32)
+    if kind == 1:
+        x[:] = x[0]                                            # constant
+    elif kind == 2:
+        x[g.random(d) < 0.5] = np.float32(-0.0)                # signed zeros
+    elif kind == 3:
+        x = np.where(g.random(d) < 0.5, -1.5, 2.25).astype(np.float32)   # two values
+    elif kind == 4:
+        x = (g.integers(-8, 8, size=d) * 0.125).astype(np.float32)       # grid values
+    elif kind == 5:
+        x = np.clip(x * 4.0, -65504, 65504).astype(np.float32)           # near the fp16 limit
+    elif kind == 6:
+        x = (g.standard_normal(d) * 1e-40).astype(np.float32)            # fp32 denormals
+    elif kind == 7:
+        x = g.laplace(0, 0.2, size=d).astype(np.float32)                  # heavy tails
+    return np.clip(x, -65504, 65504).astype(np.float32)  # the rules take fp16-range values only
+
+
+def test_oracle_matches_independent_numpy_model_on_ten_thousand_rows(oracle_lib):
+    """10800 tiny rows (d in {1, 2, 3, 4, 8, 16}, INT2/4/8, range and greedy,
+    greedy bins 1..16 and steps 0..min(bins - 1, 12)) through the C oracle and the
+    independent numpy model: packed bytes identical for every row."""
+    g = np.random.default_rng(62)
+    n_cases = 0
+    for d in (1, 2, 3, 4, 8, 16):
+        for bits in (2, 4, 8):
+            for _ in range(300):
+                x = _tiny_row(g, d)
+                Bn = int(g.integers(1, 17))
+                K = int(g.integers(0, min(Bn, 13)))  # 0 <= K < Bn, K <= 12
+                for clip in ("range", "greedy"):
+                    mode = oracle.RANGE if clip == "range" else oracle.GREEDY
+                    ours = oracle.quantize_rowwise(x[None], bits, mode, Bn, K)[0]
+                    ref = nm.encode(x, bits, clip, Bn, K)
+                    assert np.array_equal(ours, ref), (d, bits, clip, Bn, K, x)
+                    n_cases += 1
+    assert n_cases == 6 * 3 * 300 * 2 >= 10000
+
+
 def test_oracle_rejects_values_outside_fp16_range(oracle_lib):
     x = np.zeros((2, 4), np.float32)
     x[1, 2] = np.float32(70000.0)
