@@ -88,6 +88,7 @@ typedef struct ihipStream_t* qemb_stream_t; /* the same type as hipStream_t */
 #define QEMB_E_MISALIGNED -2  /* an array is not aligned as documented */
 #define QEMB_E_UNSUPPORTED -3 /* dim above QEMB_MAX_DIM */
 #define QEMB_E_LAUNCH -4      /* the HIP runtime rejected a kernel launch */
+#define QEMB_E_TOO_LARGE -5   /* n above the no-allocation entry point's maximum */
 
 #define QEMB_MAX_DIM 1024
 #define QEMB_MAX_INTERACTION_T 1024 /* tables per sample in qemb_dot_interaction */
@@ -96,6 +97,7 @@ typedef struct ihipStream_t* qemb_stream_t; /* the same type as hipStream_t */
 #define QEMB_CLIP_GREEDY 1
 
 #define QEMB_COMPRESS_VERBATIM 32 /* record header of a vector stored verbatim */
+#define QEMB_COMPRESS_NOALLOC_MAX_VECTORS (1 << 21) /* n limit of qemb_compress_pooled_noalloc */
 
 #define QEMB_BASE_SYMMETRIC 0
 #define QEMB_BASE_PERCENTILE 1
@@ -357,6 +359,25 @@ int qemb_compress_pooled(const float* x, int64_t n, int32_t dim, int32_t T, cons
 int qemb_decompress_pooled(const uint8_t* in, int64_t in_bytes, const int64_t* offs, int64_t n,
                            int32_t dim, int32_t T, const float* eb, float* y, int32_t* err_count,
                            qemb_stream_t stream);
+
+/* qemb_compress_pooled_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): qemb_compress_pooled with the same arguments, results
+ * and kernels, minus the workspace argument.  It allocates nothing: its
+ * workspace is a fixed array inside the library, 2.25 MiB per GPU, which
+ * every GPU the library runs on holds until the process ends.
+ *   n <= QEMB_COMPRESS_NOALLOC_MAX_VECTORS (2^21 vectors: two of the
+ *   multi-hot workload's pooled outputs of 16384 x 64); larger n returns
+ *   QEMB_E_TOO_LARGE before any GPU work.
+ * The caller still passes out and offs.  Every call on a GPU shares that
+ * GPU's array, which keeps the last call's contents (nothing in it needs to
+ * start at zero): calls that overlap on one GPU -- on two streams, or from
+ * two threads without ordering -- race on it and must be serialized by the
+ * caller.  The first call on a device looks up the array's address there
+ * (with the stream's device current), which is not an allocation.
+ */
+int qemb_compress_pooled_noalloc(const float* x, int64_t n, int32_t dim, int32_t T, const float* eb,
+                                 uint8_t* out, int64_t* offs, qemb_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -13,5 +13,5 @@ from .qemb import (  # noqa: F401
     interaction_width, l2_error,
     l2_error_codebook, load_library, quantize_codebook, quantize_rowwise, row_stride,
     COMPRESS_VERBATIM, compress_bound, compress_pooled, compress_record_bytes, compress_workspace_bytes,
-    decompress_pooled,
+    decompress_pooled, compress_pooled_noalloc, COMPRESS_NOALLOC_MAX_VECTORS,
 )

@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -53,6 +54,44 @@ constexpr int kBlock = 256;
 
 }  // namespace
 
+// Workspace of qemb_compress_pooled_noalloc: the per-block record sizes and
+// the per-vector widths of up to QEMB_COMPRESS_NOALLOC_MAX_VECTORS vectors.
+// In host code `scratch` is only a handle; its device address on each GPU
+// comes from hipGetSymbolAddress (scratch_device_ptr).
+constexpr int64_t kNoAllocBlocks = (QEMB_COMPRESS_NOALLOC_MAX_VECTORS + kCmpVPB - 1) / kCmpVPB;
+constexpr size_t kNoAllocScratchBytes =
+    8 * kNoAllocBlocks + ((QEMB_COMPRESS_NOALLOC_MAX_VECTORS + 15) / 16) * 16;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device (null until looked up)
+
+// The device address of `scratch` on the device of `st` (the current device
+// for the null stream), looked up once per device with that device current.
+int scratch_device_ptr(hipStream_t st, void** ptr) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return QEMB_E_LAUNCH;
+  int dev = cur;
+  if (st != nullptr && hipStreamGetDevice(st, &dev) != hipSuccess) return QEMB_E_INVALID_ARG;
+  if (dev < 0 || dev >= kMaxDevices) return QEMB_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return QEMB_E_LAUNCH;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return QEMB_E_LAUNCH;
+    if (e != hipSuccess || p == nullptr) return QEMB_E_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return QEMB_OK;
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------
 // C ABI
 // ---------------------------------------------------------------------------
@@ -68,6 +107,7 @@ const char* qemb_strerror(int code) {
     case QEMB_E_MISALIGNED: return "array not 16-byte aligned";
     case QEMB_E_UNSUPPORTED: return "unsupported size";
     case QEMB_E_LAUNCH: return "kernel launch failed";
+    case QEMB_E_TOO_LARGE: return "more vectors than the no-allocation entry point's maximum";
     default: return "unknown error";
   }
 }
@@ -386,6 +426,24 @@ int qemb_compress_pooled(const float* x, int64_t n, int32_t dim, int32_t T, cons
   int64_t* bsum = reinterpret_cast<int64_t*>(workspace);
   uint8_t* wbuf = reinterpret_cast<uint8_t*>(workspace) + 8 * nblk;
   return dispatch_compress(x, n, dim, T, eb, out, offs, bsum, wbuf, reinterpret_cast<hipStream_t>(stream));
+}
+
+int qemb_compress_pooled_noalloc(const float* x, int64_t n, int32_t dim, int32_t T, const float* eb,
+                                 uint8_t* out, int64_t* offs, qemb_stream_t stream) {
+  if (n < 0 || dim < 1 || T < 1) return QEMB_E_INVALID_ARG;
+  if (n > QEMB_COMPRESS_NOALLOC_MAX_VECTORS) return QEMB_E_TOO_LARGE;
+  if (dim > QEMB_MAX_DIM) return QEMB_E_UNSUPPORTED;
+  if (!offs || (n > 0 && (!x || !eb || !out))) return QEMB_E_INVALID_ARG;
+  if ((x && !aligned16(x)) || ((uintptr_t)out & 3u) || ((uintptr_t)offs & 7u) || ((uintptr_t)eb & 3u))
+    return QEMB_E_MISALIGNED;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  const int rc = scratch_device_ptr(st, &ws);
+  if (rc != QEMB_OK) return rc;
+  const int64_t nblk = (n + kCmpVPB - 1) / kCmpVPB;  // <= kNoAllocBlocks
+  int64_t* bsum = reinterpret_cast<int64_t*>(ws);
+  uint8_t* wbuf = reinterpret_cast<uint8_t*>(ws) + 8 * nblk;
+  return dispatch_compress(x, n, dim, T, eb, out, offs, bsum, wbuf, st);
 }
 
 int qemb_decompress_pooled(const uint8_t* in, int64_t in_bytes, const int64_t* offs, int64_t n,

@@ -29,7 +29,7 @@ EXPORTED = (
     "qemb_bag_forward_codebook", "qemb_l2_error_codebook", "qemb_interaction_width",
     "qemb_dot_interaction", "qemb_quantize_baseline", "qemb_compress_record_bytes",
     "qemb_compress_bound", "qemb_compress_workspace_bytes", "qemb_compress_pooled",
-    "qemb_decompress_pooled",
+    "qemb_decompress_pooled", "qemb_compress_pooled_noalloc",
 )
 
 COMPRESS_VERBATIM = 32  # record header of a vector stored verbatim
@@ -115,6 +115,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.qemb_compress_pooled.restype = ctypes.c_int
     L.qemb_decompress_pooled.argtypes = [p, i64, p, i64, i32, i32, p, p, p, p]
     L.qemb_decompress_pooled.restype = ctypes.c_int
+    L.qemb_compress_pooled_noalloc.argtypes = [p, i64, i32, i32, p, p, p, p]
+    L.qemb_compress_pooled_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -454,6 +456,29 @@ def compress_pooled(x: torch.Tensor, eb: torch.Tensor, T: Optional[int] = None,
         raise ValueError("out, offs or workspace too small")
     _check("qemb_compress_pooled", load_library().qemb_compress_pooled(
         _ptr(x), n, dim, T, _ptr(eb), _ptr(out), _ptr(offs), _ptr(workspace), _stream(x)))
+    return out, offs
+
+
+COMPRESS_NOALLOC_MAX_VECTORS = 1 << 21
+
+
+def compress_pooled_noalloc(x: torch.Tensor, eb: torch.Tensor, out: torch.Tensor, offs: torch.Tensor,
+                            T: Optional[int] = None):
+    """compress_pooled for callers that cannot allocate: the library's
+    workspace is a fixed per-GPU array (at most COMPRESS_NOALLOC_MAX_VECTORS
+    vectors), and out (compress_bound(n, d) bytes) and offs ([n + 1] int64)
+    are the caller's.  Calls that overlap on one GPU race on the array."""
+    _dev("x", x, torch.float32)
+    _dev("eb", eb, torch.float32)
+    _dev("out", out, torch.uint8)
+    _dev("offs", offs, torch.int64)
+    n, T, dim = _vectors(x, T)
+    if eb.numel() != T:
+        raise ValueError("eb must hold %d bounds" % T)
+    if out.numel() < compress_bound(n, dim) or offs.numel() != n + 1:
+        raise ValueError("out or offs too small")
+    _check("qemb_compress_pooled_noalloc", load_library().qemb_compress_pooled_noalloc(
+        _ptr(x), n, dim, T, _ptr(eb), _ptr(out), _ptr(offs), _stream(x)))
     return out, offs
 
 

@@ -256,3 +256,14 @@ def test_library_from_other_sources_is_refused(tmp_path, lib):
     os.remove(str(stale) + ".srchash")
     with pytest.raises(qemb.QembError, match="other kernel sources"):
         qemb.check_built_from_current_source(str(stale))
+
+
+def test_noalloc_compression_refuses_too_many_vectors_before_gpu_work(lib):
+    """qemb_compress_pooled_noalloc checks n against its fixed workspace
+    before any GPU call (the pointers are never touched here)."""
+    from int4_row_wise_amd import qemb
+    n = qemb.COMPRESS_NOALLOC_MAX_VECTORS + 1
+    rc = lib.qemb_compress_pooled_noalloc(256, n, 32, 1, 256, 256, 256, None)
+    assert rc == -5
+    assert b"maximum" in lib.qemb_strerror(rc)
+    assert lib.qemb_compress_pooled_noalloc(256, -1, 32, 1, 256, 256, 256, None) == -1
