@@ -61,6 +61,8 @@ def parse():
                     help="error-bounded compression of the pooled output only")
     ap.add_argument("--interaction-only", action="store_true",
                     help="only one INT4 lookup and the dot interaction on its output (for profiling)")
+    ap.add_argument("--gather-floor", action="store_true",
+                    help="only the INT4 lookup and the gather floor of its memory traffic")
     ap.add_argument("--quantizer-only", action="store_true",
                     help="only the quantizer workload (for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -524,6 +526,57 @@ def oracle_quantizer_rates(oracle, x_np, bits, mode, n_bins, n_steps, n_all, n_o
             "dequantize": oracle_rate(oracle, deq, min(n_all * 4, packed.shape[0]), n_one)}
 
 
+def gather_floor(q, torch, packed, w, batches, out, dev, runs=(16, 32), steps=20, warmup=3):
+    """The memory traffic of the INT4 lookup with none of its arithmetic
+    (libqemb_floor.so: every id and weight read once, contiguously; every row
+    read as the lookup reads it, 8 lanes x 12 bytes; the output's bytes
+    written), over the same table and rotating batches: a floor for any
+    kernel that reads rows this way.  `runs`: batches of 64 ids per wave."""
+    import ctypes
+    from int4_row_wise_amd import build as qbuild
+    lib = ctypes.CDLL(qbuild.FLOOR_LIB)
+    p, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.qemb_floor_gather.argtypes = [p, i64, p, p, p, p, i64, p, p, i32, p, i64, i64, p, p]
+    lib.qemb_floor_gather.restype = ctypes.c_int
+    T, B = w.n_tables, w.batch
+    toff = to_dev(torch, np.array([0] + list(np.cumsum(w.rows)), dtype=np.int64), dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out_bytes = out.numel() * 4
+    res = {}
+    for run in runs:
+        plans = []
+        for b in batches:
+            id_start = b["offs_np"][::B].astype(np.int64)  # table t's ids start at offsets[t * B]
+            waves = -(-(id_start[1:] - id_start[:-1]) // (64 * run))
+            wave_start = np.concatenate([[0], np.cumsum(waves)]).astype(np.int64)
+            n_waves = int(wave_start[-1])
+            store = -(-out_bytes // (n_waves * run) // 512) * 512  # output bytes per batch of 64 ids
+            plans.append((to_dev(torch, id_start, dev), to_dev(torch, np.repeat(np.arange(T, dtype=np.int32), waves), dev),
+                          to_dev(torch, wave_start, dev), n_waves, b, store * run))
+        st = torch.cuda.current_stream().cuda_stream
+
+        def call(k):
+            ids_start, wave_table, wave_start, n_waves, b, opw = plans[k % len(plans)]
+            rc = lib.qemb_floor_gather(packed.data_ptr(), packed.shape[1], toff.data_ptr(), ids_start.data_ptr(),
+                                       wave_table.data_ptr(), wave_start.data_ptr(), n_waves, b["idx"].data_ptr(),
+                                       b["w"].data_ptr(), run, out.data_ptr(), out_bytes, opw, sink.data_ptr(), st)
+            assert rc == 0, rc
+        for k in range(warmup):
+            call(k)
+        torch.cuda.synchronize()
+        tm = Timer(torch)
+        for k in range(steps):
+            with tm:
+                call(k)
+        ms = tm.ms()
+        nnz = float(np.mean([batches[k % len(batches)]["nnz"] for k in range(steps)]))
+        byt = algorithmic_bag_bytes(int(nnz), T * B, w.dim, 4, 4, True)
+        res["run_%d_bags_per_wave_eq_%d" % (run, run * 2)] = {
+            "avg_launch_ms": float(np.mean(ms)), "median_ms": float(np.median(ms)),
+            "GBps": byt / (np.mean(ms) * 1e-3) / 1e9, "hbm_frac": byt / (np.mean(ms) * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
 def ctr_extras(q, synth, torch, oracle, dev, wid, steps=50, warmup=5, with_oracle=True):
     """A one-hot workload end to end: every table drawn on the GPU and
     quantized by the library (timed per chunk of at most 2^24 rows; HIP
@@ -652,7 +705,8 @@ def main():
         print(json.dumps({"quantizer": quantizer_extras(q, synth, torch, dev)}), flush=True)
         return
     w = synth.workload(4)
-    bits_list = (4,) if (args.no_extras or args.interaction_only or args.compress_only) else (4, 8)
+    bits_list = (4,) if (args.no_extras or args.interaction_only or args.compress_only or
+                         args.gather_floor) else (4, 8)
 
     t0 = time.time()
     packed = {} if args.codebook_only else build_table(q, synth, torch, w, bits_list, dev)
@@ -686,6 +740,12 @@ def main():
         print(json.dumps({"codebook": res, "workload": w.name}), flush=True)
         return
 
+    if args.gather_floor:
+        ms, _ = bench_bags(q, torch, packed[4], toff, batches, w, 4, args.steps, args.warmup, out)
+        floor = gather_floor(q, torch, packed[4], w, batches, out, dev, steps=args.steps)
+        print(json.dumps({"lookup_avg_launch_ms": float(np.mean(ms)), "gather_floor": floor,
+                          "workload": w.name}), flush=True)
+        return
     ms, wall = bench_bags(q, torch, packed[4], toff, batches, w, 4, args.steps, args.warmup, out)
     nnz_timed = sum(batches[k % len(batches)]["nnz"] for k in range(args.steps))
     bytes_timed = sum(algorithmic_bag_bytes(batches[k % len(batches)]["nnz"], n_bags, w.dim, 4, 4,
@@ -757,6 +817,8 @@ def main():
             "hbm_frac": b0 / (np.median(msc) * 1e-3) / 1e9 / HBM_PEAK_GBS}
         result["interaction"] = interaction_extras(q, torch, out, w, dev)
         result["compress"] = compress_extras(q, torch, out, dev)
+        # (after the consumers of the pooled output: the floor overwrites it)
+        result["gather_floor"] = gather_floor(q, torch, packed[4], w, batches, out, dev)
         # 2-bit rows of the same tables (range), same batches
         p2 = build_table(q, synth, torch, w, (2,), dev)[2]
         ms2, _ = bench_bags(q, torch, p2, toff, batches, w, 2, 10, 3, out)

@@ -19,6 +19,9 @@ SRC = os.path.join(CSRC, "qemb.hip")  # the translation unit; it includes the cs
 HEADER = os.path.join(ROOT, "include", "qemb.h")
 LIB = os.path.join(HERE, "libqemb.so")
 LIB_HASH = LIB + ".srchash"  # source sha256 recorded at build time
+# the gather floor (a measurement aid for bench.py, not part of the C ABI)
+FLOOR_SRC = os.path.join(CSRC, "gather_floor.hip")
+FLOOR_LIB = os.path.join(HERE, "libqemb_floor.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
@@ -39,16 +42,22 @@ def build(force: bool = True, verbose: bool = False) -> str:
     if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(
             [os.path.getmtime(f) for f in source_files()] + [os.path.getmtime(HEADER)]):
         return LIB
+    # the floor (one small kernel) compiles beside the library
+    floor_tmp = FLOOR_LIB + ".tmp%d" % os.getpid()
+    floor = subprocess.Popen([hipcc(), *HIPCC_FLAGS, "-o", floor_tmp, FLOOR_SRC], stdout=subprocess.PIPE,
+                             stderr=subprocess.STDOUT, text=True)
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
+    floor_out, _ = floor.communicate()
+    out = "\n".join(l for l in (r.stdout + floor_out).splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0 or floor.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + out)
     if out.strip() and verbose:
         print(out)
+    os.replace(floor_tmp, FLOOR_LIB)
     os.replace(tmp, LIB)
     with open(LIB_HASH, "w") as f:
         f.write(source_sha256() + "\n")
@@ -56,7 +65,8 @@ def build(force: bool = True, verbose: bool = False) -> str:
 
 
 def source_files() -> list:
-    """qemb.hip and the parts it includes, in a fixed order."""
+    """The kernel sources: qemb.hip, the parts it includes and the gather
+    floor, in a fixed order."""
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".inc")))
 
 
