@@ -38,8 +38,8 @@ MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
 # the counters show more than one wave64 VALU instruction per CU per cycle,
 # so the 128 lanes per CU per clock are two wave64 instructions)
 VALU_PEAK_LANE_INSTS = 256 * 128 * 2.4e9
-HEADLINE_KERNEL = "bag_stream_kernel<4, 8, int, true, true, true>"
-COUNTERS = os.path.join(ROOT, "profiles", "bag_stream_int4_multihot_counters.md")
+HEADLINE_KERNEL = "bag_seg_kernel<int, true, 24, 2>"
+COUNTERS = os.path.join(ROOT, "profiles", "bag_seg_int4_multihot_counters.md")
 QUANT_COUNTERS = os.path.join(ROOT, "profiles", "quantizer_workload_counters.md")
 
 

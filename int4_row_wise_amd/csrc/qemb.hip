@@ -9,6 +9,9 @@
 //                             bags, pipelined over batches of ids
 //   * bag_pack_kernel         the same over runs of 64 bags whose ids are packed
 //                             into full batches (bags of a few to a few tens of ids)
+//   * bag_seg_kernel          the same for INT4 rows of 64 code bytes: runs of
+//                             bags cut into equal chunks per row group, bag sums
+//                             kept in LDS
 //   * bag_wave_kernel         the same for rows wider than 8 lanes
 //   * bag_slice_kernel        the same for short bags, several bags per wave
 //   * l2_partial/l2_final     normalized l2 error, fixed-order reduction
@@ -45,6 +48,7 @@ constexpr int kBlock = 256;
 #include "quantize.inc"
 #include "lookup.inc"
 #include "pack.inc"
+#include "seg.inc"
 #include "l2_error.inc"
 #include "baselines.inc"
 #include "codebook.inc"
@@ -195,7 +199,9 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
   a.vec4 = (dim % 4 == 0);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // Kernel choice by row width (lanes of 16 codes per row) and mean bag
-  // length, from timings of the three bag kernels over bag-length mixes:
+  // length, from timings of the bag kernels over bag-length mixes:
+  //   INT4 rows of 64 code bytes, two or more ids per bag on average: runs
+  //     of 24 bags cut into equal chunks per row group, bag sums in LDS;
   //   rows of 4..8 lanes, mean length up to 16 (24 for INT4): runs of 64
   //     bags packed into full id batches;
   //   rows of 1..2 lanes, mean length up to 16, and wider rows with bags of
@@ -211,6 +217,7 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
     return dispatch_slice<2, 4>(a, next_pow2((a.C + 3) / 4), next_pow2((mean_len + kBagUnroll - 1) / kBagUnroll),
                                 st);
   }
+  if (seg_fits(a, bits) && nnz >= 2 * a.n_bags) return dispatch_seg(a, st);
   const int lpr = bits == 4 ? pack_lanes<4>(a) : pack_lanes<8>(a);
   if (lpr >= 4 && mean_len <= (bits == 4 ? 24 : 16))
     return bits == 4 ? dispatch_pack<4>(a, st) : dispatch_pack<8>(a, st);

@@ -126,9 +126,10 @@ def test_codebook_writers(q, dim):
 
 
 # (bits, dim, bag lengths lo..hi): each lookup kernel and its store paths --
-# several bags per wave (d 16, 33, 1000 short), packed runs (d 64, 100,
-# 128 short; INT2 d 97), one wave per bag (d 128, 100 long: 8 lanes; d 512,
-# 1000 long: wide rows)
+# several bags per wave (d 16, 33, 1000 short), packed runs (d 64, 100
+# short; INT2 d 97), chunked runs with bag sums in LDS (INT4 d 128, short
+# and long), one wave per bag (INT8 d 100 and INT2 d 128 long: 8 lanes;
+# d 512, 1000 long: wide rows)
 LOOKUPS = [(4, 16, 0, 6), (4, 33, 0, 6), (8, 1000, 0, 4), (4, 64, 0, 12), (4, 100, 0, 12),
            (4, 128, 0, 12), (8, 100, 0, 12), (2, 97, 0, 12), (4, 128, 30, 70), (8, 100, 30, 70),
            (2, 128, 30, 70), (4, 512, 10, 40), (8, 1000, 10, 40), (4, 16, 30, 70)]
