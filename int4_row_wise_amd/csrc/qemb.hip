@@ -9,9 +9,9 @@
 //                             bags, pipelined over batches of ids
 //   * bag_pack_kernel         the same over runs of 64 bags whose ids are packed
 //                             into full batches (bags of a few to a few tens of ids)
-//   * bag_seg_kernel          the same for INT4 rows of 64 code bytes: runs of
-//                             bags cut into equal chunks per row group, bag sums
-//                             kept in LDS
+//   * bag_seg_kernel          the same for rows of 128 codes in 8 lanes (INT4,
+//                             INT2): runs of bags cut into equal chunks per row
+//                             group, bag sums kept in LDS
 //   * bag_wave_kernel         the same for rows wider than 8 lanes
 //   * bag_slice_kernel        the same for short bags, several bags per wave
 //   * l2_partial/l2_final     normalized l2 error, fixed-order reduction
@@ -200,8 +200,9 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // Kernel choice by row width (lanes of 16 codes per row) and mean bag
   // length, from timings of the bag kernels over bag-length mixes:
-  //   INT4 rows of 64 code bytes, two or more ids per bag on average: runs
-  //     of 24 bags cut into equal chunks per row group, bag sums in LDS;
+  //   rows of 128 codes in 8 lanes (INT4 d 127..128, INT2 d 125..128), two
+  //     or more ids per bag on average: runs of 24 bags cut into equal
+  //     chunks per row group, bag sums in LDS;
   //   rows of 4..8 lanes, mean length up to 16 (24 for INT4): runs of 64
   //     bags packed into full id batches;
   //   rows of 1..2 lanes, mean length up to 16, and wider rows with bags of
@@ -209,6 +210,8 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
   //   longer bags: one wave per bag (the stream kernel up to 8 lanes per
   //     row, the wave kernel beyond).
   const int64_t mean_len = (nnz + a.n_bags - 1) / a.n_bags;
+  if (seg_fits(a, bits) && nnz >= 2 * a.n_bags)
+    return bits == 4 ? dispatch_seg<4>(a, st) : dispatch_seg<2>(a, st);
   if (bits == 2) {
     const int lpr = pack_lanes<2>(a);
     if (lpr >= 4 && mean_len <= 16) return dispatch_pack<2>(a, st);
@@ -217,7 +220,6 @@ int qemb_bag_forward(const uint8_t* packed, int64_t total_rows, const int64_t* t
     return dispatch_slice<2, 4>(a, next_pow2((a.C + 3) / 4), next_pow2((mean_len + kBagUnroll - 1) / kBagUnroll),
                                 st);
   }
-  if (seg_fits(a, bits) && nnz >= 2 * a.n_bags) return dispatch_seg(a, st);
   const int lpr = bits == 4 ? pack_lanes<4>(a) : pack_lanes<8>(a);
   if (lpr >= 4 && mean_len <= (bits == 4 ? 24 : 16))
     return bits == 4 ? dispatch_pack<4>(a, st) : dispatch_pack<8>(a, st);
