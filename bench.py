@@ -38,7 +38,7 @@ MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
 # the counters show more than one wave64 VALU instruction per CU per cycle,
 # so the 128 lanes per CU per clock are two wave64 instructions)
 VALU_PEAK_LANE_INSTS = 256 * 128 * 2.4e9
-HEADLINE_KERNEL = "bag_seg_kernel<int, true, 24, 2>"
+HEADLINE_KERNEL = "bag_seg_kernel<4, int, true, 24, 2>"
 COUNTERS = os.path.join(ROOT, "profiles", "bag_seg_int4_multihot_counters.md")
 QUANT_COUNTERS = os.path.join(ROOT, "profiles", "quantizer_workload_counters.md")
 
@@ -263,6 +263,43 @@ def device_copy_gbps(torch, dev, nbytes=1 << 30, reps=10):
     ms = float(np.median(tm.ms()))
     del a, b
     return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def stream_ceiling(torch, dev, nbytes=2 << 30, reps=10):
+    """HBM rates of the plainest access patterns on this GPU (libqemb_floor.so:
+    16-byte non-temporal loads and stores, u words per lane and round, a
+    grid-stride loop): read only, write only, and a copy (read + write
+    bytes), GB/s of the median launch over `nbytes` per array, the best of a
+    few launch shapes (workgroups, u)."""
+    import ctypes
+    from int4_row_wise_amd import build as qbuild
+    lib = ctypes.CDLL(qbuild.FLOOR_LIB)
+    p, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.qemb_floor_stream.argtypes = [p, p, ctypes.c_int64, i32, i32, i32, p, p]
+    lib.qemb_floor_stream.restype = ctypes.c_int
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    b = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    n = nbytes // 16
+    res = {"bytes_per_array": nbytes}
+    for mode, name, moved in ((0, "read", nbytes), (1, "write", nbytes), (2, "copy", 2 * nbytes)):
+        best = (0.0, None)
+        for grid, u in ((1024, 2), (4096, 4), (8192, 8), (16384, 4)):
+            def call():
+                rc = lib.qemb_floor_stream(a.data_ptr(), b.data_ptr(), n, mode, grid, u, sink.data_ptr(), st)
+                assert rc == 0, rc
+            call()
+            torch.cuda.synchronize()
+            tm = Timer(torch)
+            for _ in range(reps):
+                with tm:
+                    call()
+            rate = moved / (float(np.median(tm.ms())) * 1e-3) / 1e9
+            best = max(best, (rate, "%d workgroups, %d words per lane" % (grid, u)), key=lambda x: x[0])
+        res[name + "_GBps"], res[name + "_shape"] = best
+    del a, b
+    return res
 
 
 def bench_cold(q, torch, packed, toff, batch, w, bits, out, dev, reps=5):
@@ -815,6 +852,7 @@ def main():
             "note": "each launch after writing a 1 GiB scratch buffer (L2 and MALL flushed)",
             "launch_ms": launch_stats(msc), "GBps": b0 / (np.median(msc) * 1e-3) / 1e9,
             "hbm_frac": b0 / (np.median(msc) * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        result["stream_ceiling"] = stream_ceiling(torch, dev)
         result["interaction"] = interaction_extras(q, torch, out, w, dev)
         result["compress"] = compress_extras(q, torch, out, dev)
         # (after the consumers of the pooled output: the floor overwrites it)

@@ -1,5 +1,6 @@
 // gather_floor.hip -- libqemb_floor.so, a measurement aid beside libqemb.so
-// (not part of the library's C ABI; bench.py --gather-floor runs it).
+// (not part of the library's C ABI; bench.py --gather-floor runs it, and
+// every bench run times its streaming ceilings, at the end of this file).
 //
 // The memory traffic of one pooled lookup call over packed rows of up to 8
 // lanes x 8 code bytes (INT4 rows of d <= 128), with none of its arithmetic:
@@ -112,6 +113,51 @@ __global__ __launch_bounds__(kWPB * kWave) void gather_floor_kernel(
   if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads live
 }
 
+// Streaming ceilings: HBM rates of the plainest access patterns, for the
+// rooflines of the streaming kernels.  mode 0 reads n 16-byte words (folded
+// into one word per workgroup), mode 1 writes them, mode 2 copies them; each
+// lane moves U words per round with non-temporal loads and stores, rounds
+// strided over the whole grid.
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+template <int U>
+__global__ __launch_bounds__(256) void stream_ceiling_kernel(const v4u* __restrict__ in, v4u* __restrict__ out,
+                                                             int64_t n, int mode, uint32_t* __restrict__ sink) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (U - 1) * stride < n; i += U * stride) {
+    if (mode == 1) {
+#pragma unroll
+      for (int r = 0; r < U; ++r) __builtin_nontemporal_store(v4u{(unsigned)r, 0u, 0u, 0u}, out + i + r * stride);
+    } else {
+      v4u v[U];
+#pragma unroll
+      for (int r = 0; r < U; ++r) v[r] = __builtin_nontemporal_load(in + i + r * stride);
+      if (mode == 2) {
+#pragma unroll
+        for (int r = 0; r < U; ++r) __builtin_nontemporal_store(v[r], out + i + r * stride);
+      } else {
+#pragma unroll
+        for (int r = 0; r < U; ++r) acc ^= v[r].x ^ v[r].y ^ v[r].z ^ v[r].w;
+      }
+    }
+  }
+  for (; i < n; i += stride) {
+    if (mode == 1) {
+      out[i] = v4u{0u, 0u, 0u, 0u};
+    } else {
+      const v4u v = in[i];
+      if (mode == 2) {
+        out[i] = v;
+      } else {
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+      }
+    }
+  }
+  if (mode == 0 && acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads live
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,6 +184,28 @@ int qemb_floor_gather(const uint8_t* packed, int64_t S, const int64_t* table_off
   hipLaunchKernelGGL(gather_floor_kernel, dim3((unsigned)blocks), dim3(kWPB * kWave), 0, stream, packed, S,
                      table_offsets, id_start, wave_table, wave_start, n_waves, ids, weights, (int)run, out,
                      out_bytes, out_bytes_per_wave, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// Launch the streaming-ceiling kernel (see above) on `grid` workgroups of
+// 256 lanes with u (2, 4 or 8) words per lane and round: in and out device
+// arrays of n 16-byte words (in unused for mode 1, out for mode 0), sink one
+// uint32.  Returns 0, -1 on bad arguments, -4 if the launch failed.
+int qemb_floor_stream(const void* in, void* out, int64_t n, int32_t mode, int32_t grid, int32_t u, uint32_t* sink,
+                      hipStream_t stream) {
+  if (n < 0 || mode < 0 || mode > 2 || grid < 1 || !sink || (mode != 1 && !in) || (mode != 0 && !out) ||
+      (u != 2 && u != 4 && u != 8))
+    return -1;
+  if (n == 0) return 0;
+  const v4u* src = static_cast<const v4u*>(in);
+  v4u* dst = static_cast<v4u*>(out);
+  if (u == 2) {
+    hipLaunchKernelGGL(stream_ceiling_kernel<2>, dim3(grid), dim3(256), 0, stream, src, dst, n, (int)mode, sink);
+  } else if (u == 4) {
+    hipLaunchKernelGGL(stream_ceiling_kernel<4>, dim3(grid), dim3(256), 0, stream, src, dst, n, (int)mode, sink);
+  } else {
+    hipLaunchKernelGGL(stream_ceiling_kernel<8>, dim3(grid), dim3(256), 0, stream, src, dst, n, (int)mode, sink);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
