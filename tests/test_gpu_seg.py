@@ -121,6 +121,32 @@ def test_chunked_runs_one_bag_across_every_group(q, bits):
     _check(q, packed, bt, 128, np.int64, "bags across every group, int64 ids", bits=bits)
 
 
+@pytest.mark.parametrize("bits", [4, 2])
+def test_chunked_runs_starting_off_the_8_id_grid(q, bits):
+    """Runs whose first CSR position takes every value mod 8 and whose first
+    bag (1000 ids) covers the first chunks entirely: the chunks are counted
+    from the 8-id boundary below the run, so group 0's chunk starts before
+    the run and holds no bag end (the case where the slot count to the
+    chunk's 'no end' marker must not overflow)."""
+    g = np.random.default_rng(9750 + bits)
+    runs = 9
+    lens = []
+    pos = 0
+    for r in range(runs):
+        run = [1000] + [2] * 22
+        pos += sum(run)
+        last = 2 + ((r + 1 - (pos + 2)) % 8)  # the next run starts at position r + 1 (mod 8)
+        run.append(last)
+        pos += last
+        lens += run
+    lens = np.array(lens, np.int64)
+    starts = np.concatenate([[0], np.cumsum(lens)])[::24][:runs]
+    assert sorted(int(x) % 8 for x in starts) == list(range(8)) + [0]
+    packed, bt = _case(g, 128, 1, lens.size, [300], lens, True, bits)
+    for itype in (np.int32, np.int64):
+        _check(q, packed, bt, 128, itype, "runs off the 8-id grid, %s" % itype.__name__, bits=bits)
+
+
 @pytest.mark.parametrize("bits,dim", SHAPES)
 def test_chunked_runs_invalid_ids_offsets_and_tables(q, bits, dim):
     """Ids outside their table, decreasing offsets, offsets past nnz and a
