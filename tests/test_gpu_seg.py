@@ -141,7 +141,7 @@ def test_chunked_runs_starting_off_the_8_id_grid(q, bits):
         lens += run
     lens = np.array(lens, np.int64)
     starts = np.concatenate([[0], np.cumsum(lens)])[::24][:runs]
-    assert sorted(int(x) % 8 for x in starts) == list(range(8)) + [0]
+    assert [int(x) % 8 for x in starts] == [0, 1, 2, 3, 4, 5, 6, 7, 0]
     packed, bt = _case(g, 128, 1, lens.size, [300], lens, True, bits)
     for itype in (np.int32, np.int64):
         _check(q, packed, bt, 128, itype, "runs off the 8-id grid, %s" % itype.__name__, bits=bits)
