@@ -65,6 +65,9 @@ def parse():
                     help="only the INT4 lookup and the gather floor of its memory traffic")
     ap.add_argument("--quantizer-only", action="store_true",
                     help="only the quantizer workload (for profiling)")
+    ap.add_argument("--uniform-ids", action="store_true",
+                    help="only the INT4 lookup with ids uniform over each table (the no-reuse "
+                         "control, for profiling)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -742,8 +745,11 @@ def main():
         print(json.dumps({"quantizer": quantizer_extras(q, synth, torch, dev)}), flush=True)
         return
     w = synth.workload(4)
+    if args.uniform_ids:
+        import dataclasses
+        w = dataclasses.replace(w, alpha=None)
     bits_list = (4,) if (args.no_extras or args.interaction_only or args.compress_only or
-                         args.gather_floor) else (4, 8)
+                         args.gather_floor or args.uniform_ids) else (4, 8)
 
     # the index batches (seconds of host work) come first and the tables
     # (GPU work) right before the timed lookups: a GPU left idle for seconds
@@ -782,6 +788,15 @@ def main():
         print(json.dumps({"codebook": res, "workload": w.name}), flush=True)
         return
 
+    if args.uniform_ids:
+        ms, _ = bench_bags(q, torch, packed[4], toff, batches, w, 4, args.steps, args.warmup, out)
+        bu = algorithmic_bag_bytes(batches[0]["nnz"], n_bags, w.dim, 4, 4, True)
+        print(json.dumps({"uniform_ids_lookup": {
+            "avg_launch_ms": float(np.mean(ms)), "lookups": batches[0]["nnz"],
+            "GBps": bu / (np.mean(ms) * 1e-3) / 1e9,
+            "hbm_frac": bu / (np.mean(ms) * 1e-3) / 1e9 / HBM_PEAK_GBS}, "workload": w.name + ", uniform ids"}),
+              flush=True)
+        return
     if args.gather_floor:
         ms, _ = bench_bags(q, torch, packed[4], toff, batches, w, 4, args.steps, args.warmup, out)
         floor = gather_floor(q, torch, packed[4], w, batches, out, dev, steps=args.steps)
