@@ -42,6 +42,9 @@ def build(force: bool = True, verbose: bool = False) -> str:
     if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= max(
             [os.path.getmtime(f) for f in source_files()] + [os.path.getmtime(HEADER)]):
         return LIB
+    # the hash of the sources as compiled: taken before the compiler reads
+    # them, so an edit made while it runs cannot be recorded for this build
+    src_hash = source_sha256()
     # the floor (one small kernel) compiles beside the library
     floor_tmp = FLOOR_LIB + ".tmp%d" % os.getpid()
     floor = subprocess.Popen([hipcc(), *HIPCC_FLAGS, "-o", floor_tmp, FLOOR_SRC], stdout=subprocess.PIPE,
@@ -60,7 +63,7 @@ def build(force: bool = True, verbose: bool = False) -> str:
     os.replace(floor_tmp, FLOOR_LIB)
     os.replace(tmp, LIB)
     with open(LIB_HASH, "w") as f:
-        f.write(source_sha256() + "\n")
+        f.write(src_hash + "\n")
     return LIB
 
 
