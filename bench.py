@@ -38,7 +38,7 @@ MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
 # the counters show more than one wave64 VALU instruction per CU per cycle,
 # so the 128 lanes per CU per clock are two wave64 instructions)
 VALU_PEAK_LANE_INSTS = 256 * 128 * 2.4e9
-HEADLINE_KERNEL = "bag_seg_kernel<4, int, true, 24, 2>"
+HEADLINE_KERNEL = "bag_seg_kernel<4, int, true, 24, 1>"
 COUNTERS = os.path.join(ROOT, "profiles", "bag_seg_int4_multihot_counters.md")
 QUANT_COUNTERS = os.path.join(ROOT, "profiles", "quantizer_workload_counters.md")
 
